@@ -1,0 +1,228 @@
+"""Pins for oracle.quant: hand-worked tiles, invariants the method fixes,
+metamorphic relations, and each fp32 step against exact rational arithmetic."""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from fp8_fine_grained_amd import workloads
+from oracle import e4m3, quant
+from tests.exact import e4m3_values_torch, round_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "quant_tiles_handworked.json")
+
+
+def _load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _load_golden(), ids=lambda c: c["name"])
+def test_handworked_tiles(case):
+    x = np.zeros(case["shape"], dtype=np.float32)
+    codes = np.zeros(case["shape"], dtype=np.uint8)
+    for idx, v in case["entries"]:
+        x[tuple(idx) if isinstance(idx, list) else (0, idx)] = np.float32(v)
+    for idx, c in case["expected_codes"]:
+        codes[tuple(idx) if isinstance(idx, list) else (0, idx)] = int(c, 16)
+    if case["kind"] == "act_1x128":
+        q, s = quant.quant_1x128(x)
+    else:
+        q, s = quant.quant_128x128(x)
+    want_s = [int(b, 16) for b in case["expected_scale_bits"]]
+    assert s.reshape(-1).view(np.uint32).tolist() == want_s
+    bad = np.argwhere(q != codes)
+    assert bad.size == 0, [(tuple(i), hex(q[tuple(i)]), hex(codes[tuple(i)])) for i in bad[:8]]
+
+
+def _inputs():
+    rng = np.random.default_rng(21)
+    t = workloads.quant_act(seed=3, M=64, K=384).float().numpy()
+    n = workloads.dense(seed=2, M=64, N=256, K=384)["x"].float().numpy()
+    tiny = workloads.tiny()["x"].numpy()
+    u = rng.uniform(-3, 3, size=(64, 384)).astype(np.float32)
+    return {"student_t": t, "normal_outliers": n, "tiny": tiny, "uniform": u}
+
+
+INPUTS = _inputs()
+DEC = np.array(e4m3_values_torch())  # independent decoder for the checks below
+
+
+def _qdq_check(x, q, s_full):
+    """Quantise-dequantise error: <= 2^-4 |x| in the normal range, <= 2^-10 s below it."""
+    deq = DEC[q] * s_full
+    err = np.abs(deq - x.astype(np.float64))
+    normal = np.abs(x) >= (2.0 ** -6) * s_full
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(x[normal]))
+    assert np.all(err[~normal] <= 2.0 ** -10 * s_full[~normal] * (1 + 2.0 ** -20))
+
+
+@pytest.mark.parametrize("name", list(INPUTS))
+def test_act_invariants(name):
+    x = INPUTS[name]
+    q, s = quant.quant_1x128(x)
+    M, K = x.shape
+    assert q.dtype == np.uint8 and s.dtype == np.float32 and s.shape == (M, K // 128)
+    assert not np.any((q & 0x7F) == 0x7F), "NaN code produced"
+    xt = x.reshape(M, K // 128, 128)
+    qt = q.reshape(M, K // 128, 128)
+    amax = np.abs(xt).max(axis=2)
+    # the group maximum always lands on the largest finite code
+    at_max = np.abs(xt) == amax[..., None]
+    assert np.all((qt[at_max] & 0x7F) == 0x7E)
+    # codes other than at the maximum never exceed it
+    assert np.all((qt & 0x7F) <= 0x7E)
+    # scale is amax/448 to within fp32 rounding
+    assert np.allclose(s, amax / 448.0, rtol=2.0 ** -23, atol=0)
+    _qdq_check(x, q, np.repeat(s.astype(np.float64), 128, axis=1))
+
+
+@pytest.mark.parametrize("name", list(INPUTS))
+def test_weight_invariants(name):
+    x = INPUTS[name][:64, :256]
+    x = np.concatenate([x, x[::-1] * np.float32(0.5)], axis=0)  # [128, 256]
+    q, s = quant.quant_128x128(x)
+    assert s.shape == (1, 2)
+    for j in range(2):
+        blk = x[:, 128 * j: 128 * (j + 1)]
+        qb = q[:, 128 * j: 128 * (j + 1)]
+        amax = np.abs(blk).max()
+        assert np.all((qb[np.abs(blk) == amax] & 0x7F) == 0x7E)
+    se = np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1)
+    _qdq_check(x, q, se)
+
+
+@pytest.mark.parametrize("j", [-20, -3, -1, 1, 5, 30])
+def test_power_of_two_equivariance(j):
+    x = INPUTS["normal_outliers"]
+    q0, s0 = quant.quant_1x128(x)
+    q1, s1 = quant.quant_1x128(x * np.float32(2.0 ** j))
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, s0 * np.float32(2.0 ** j))
+    w = x[:, :256].reshape(128, 128)
+    a0, t0 = quant.quant_128x128(w)
+    a1, t1 = quant.quant_128x128(w * np.float32(2.0 ** j))
+    assert np.array_equal(a0, a1) and np.array_equal(t1, t0 * np.float32(2.0 ** j))
+
+
+def test_sign_symmetry():
+    x = INPUTS["student_t"]
+    q0, s0 = quant.quant_1x128(x)
+    q1, s1 = quant.quant_1x128(-x)
+    assert np.array_equal(q1, q0 ^ 0x80) and np.array_equal(s0, s1)
+
+
+def test_identity_on_e4m3_exact_tiles():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(32, 256)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3C
+    codes[:, 0] = 0x7E
+    codes[:, 128] = 0xFE
+    x = DEC[codes].astype(np.float32)
+    q, s = quant.quant_1x128(x)
+    assert np.all(s == 1.0)
+    assert np.array_equal(q, codes)
+
+
+def test_group_locality():
+    x = INPUTS["uniform"].copy()
+    q0, s0 = quant.quant_1x128(x)
+    x[7, 200] = 1000.0  # row 7, group 1
+    q1, s1 = quant.quant_1x128(x)
+    ds = np.argwhere(s0 != s1)
+    assert ds.tolist() == [[7, 1]]
+    dq = np.argwhere(q0 != q1)
+    assert np.all(dq[:, 0] == 7) and np.all((dq[:, 1] >= 128) & (dq[:, 1] < 256))
+    w = INPUTS["uniform"][:, :256].reshape(128, 128).copy()
+    w = np.concatenate([w, w], axis=1)  # [128, 256]: blocks (0,0), (0,1)
+    a0, t0 = quant.quant_128x128(w)
+    w[3, 250] = -1000.0
+    a1, t1 = quant.quant_128x128(w)
+    assert t0[0, 0] == t1[0, 0] and t0[0, 1] != t1[0, 1]
+    assert np.array_equal(a0[:, :128], a1[:, :128])
+
+
+def test_ragged_groups_cover_the_columns_present():
+    x = INPUTS["student_t"][:, :300]
+    q, s = quant.quant_1x128(x)
+    assert s.shape == (64, 3)
+    q2, s2 = quant.quant_1x128(np.ascontiguousarray(x[:, 256:]))
+    assert np.array_equal(q[:, 256:], q2) and np.array_equal(s[:, 2:], s2)
+
+
+def test_along_rows_is_the_transpose_case():
+    x = INPUTS["normal_outliers"][:, :256]
+    q, s = quant.quant_1x128_along_rows(np.ascontiguousarray(x.T))
+    q2, s2 = quant.quant_1x128(x)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+def _near_midpoint_rows():
+    """Rows whose elements sit within a few fp32 ulps of s * (E4M3 midpoint).
+
+    Each row's first element fixes amax (a value whose scale 1/s is not a
+    power of two), the rest are placed where rounding x*inv and x/s can
+    disagree about which side of a midpoint y falls on."""
+    rows = []
+    grid = e4m3.DECODE_TABLE[:0x7F]
+    mids = ((grid[:-1] + grid[1:]) / 2)[8::4]  # normal-range midpoints
+    for amax in (1.0, 3.0, 0.7, 5.0e-3):
+        s = np.float32(amax) / np.float32(448)
+        xs = []
+        for mid in mids:
+            base = np.float32(mid * float(s))
+            v = base
+            for _ in range(2):
+                v = np.nextafter(v, np.float32(-1))
+            for _ in range(5):
+                xs.append(v)
+                v = np.nextafter(v, np.float32(1))
+        xs = [x for x in xs if abs(x) < amax][:127]
+        row = np.zeros(384, np.float32)
+        row[0] = amax
+        row[1:1 + len(xs)] = xs
+        rows.append(row)
+    return np.stack(rows)
+
+
+def test_fp32_steps_against_exact_arithmetic():
+    """s, inv and y = x*inv each rounded once in binary32, checked with rationals.
+
+    Also confirms the rule is x*(1/s), not x/s: the set contains elements where
+    the two round to different codes, and the oracle follows x*(1/s)."""
+    x = np.concatenate([INPUTS["student_t"][:8], INPUTS["uniform"][:8], _near_midpoint_rows()])
+    q, s = quant.quant_1x128(x)
+    grid_mid = [Fraction(v) for v in e4m3_values_torch()[:0x7F]]
+
+    def code_of(y):
+        a = min(abs(y), Fraction(448))
+        best = min(range(0x7F), key=lambda c: (abs(a - grid_mid[c]), c % 2))
+        return best | (0x80 if y < 0 else 0)
+
+    differs = 0
+    for m in range(x.shape[0]):
+        for g in range(x.shape[1] // 128):
+            tile = [Fraction(float(v)) for v in x[m, 128 * g: 128 * (g + 1)]]
+            amax = max(abs(v) for v in tile)
+            s_ex = round_f32(amax / 448)
+            assert Fraction(float(s[m, g])) == s_ex
+            inv = round_f32(1 / s_ex) if s_ex else Fraction(0)
+            for i in range(0, 128, 3 if m < 16 else 1):
+                c_mul = code_of(round_f32(tile[i] * inv))
+                c_div = code_of(round_f32(tile[i] / s_ex)) if s_ex else c_mul
+                assert q[m, 128 * g + i] == c_mul
+                differs += c_mul != c_div
+    assert differs > 0, "test set should contain elements where x*inv and x/s differ"
+
+
+def test_out_of_contract_inputs_raise():
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0] = np.float32(1e-38)
+    with pytest.raises(ValueError):
+        quant.quant_1x128(x)
+    x[0, 0] = np.inf
+    with pytest.raises(ValueError):
+        quant.quant_1x128(x)
