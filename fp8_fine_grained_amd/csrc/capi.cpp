@@ -1,0 +1,127 @@
+// C-ABI entry points declared in include/fp8fg.h: argument validation on the
+// host, then one kernel launch on the caller's stream.  Validation runs before
+// any HIP call, so every error path here is reachable without a GPU.
+#include "fp8fg.h"
+
+#include <cstdint>
+#include <limits>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kInt32Max = std::numeric_limits<int32_t>::max();
+
+bool aligned(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_size(int dtype) { return dtype == FP8FG_BF16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == FP8FG_F32 || d == FP8FG_BF16; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8FG_OK : FP8FG_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fp8fg_abi_version(void) { return FP8FG_ABI_VERSION; }
+
+const char* fp8fg_status_string(int status) {
+  switch (status) {
+    case FP8FG_OK: return "ok";
+    case FP8FG_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or unknown enum)";
+    case FP8FG_ERR_UNSUPPORTED: return "unsupported shape or layout (K and N must be multiples of 128; see fp8fg.h)";
+    case FP8FG_ERR_MISALIGNED: return "misaligned pointer or row pitch";
+    case FP8FG_ERR_HIP: return "HIP runtime error while launching";
+    default: return "unknown status";
+  }
+}
+
+int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                        int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  if (!valid_dtype(x_dtype) || M < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return FP8FG_OK;
+  if (K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!x || !q || !scales) return FP8FG_ERR_INVALID_ARG;
+  if (M > kInt32Max || K > kInt32Max || M * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  const int es = elem_size(x_dtype);
+  const bool bf16 = x_dtype == FP8FG_BF16;
+  if (!aligned(q, 16) || !aligned(scales, 4) || !aligned(x, 16)) return FP8FG_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (stride_k == 1 && stride_m >= K) {
+    if ((stride_m * es) % 16 != 0) return FP8FG_ERR_MISALIGNED;
+    return hip_status(fp8fg::launch_quant_act_rows(x, bf16, M, K, stride_m, q, scales, s));
+  }
+  if (stride_m == 1 && stride_k >= M) {
+    if (M % 8 != 0) return FP8FG_ERR_UNSUPPORTED;
+    if ((stride_k * es) % 16 != 0) return FP8FG_ERR_MISALIGNED;
+    return hip_status(fp8fg::launch_quant_act_cols(x, bf16, M, K, stride_k, q, scales, s));
+  }
+  if (stride_m < 0 || stride_k < 0) return FP8FG_ERR_INVALID_ARG;
+  return FP8FG_ERR_UNSUPPORTED;
+}
+
+int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                             uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  if (!valid_dtype(w_dtype) || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return FP8FG_OK;
+  if (N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!w || !q || !scales) return FP8FG_ERR_INVALID_ARG;
+  if (ld_w < K) return FP8FG_ERR_INVALID_ARG;
+  if ((N / 128) * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 4) || (ld_w * elem_size(w_dtype)) % 16 != 0)
+    return FP8FG_ERR_MISALIGNED;
+  return hip_status(fp8fg::launch_quant_weight(w, w_dtype == FP8FG_BF16, N, K, ld_w, q, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                      int accum, const void* y, int y_dtype, int64_t M, int64_t N, int64_t K) {
+  if (!valid_dtype(y_dtype) || M < 0 || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (accum != FP8FG_ACCUM_FP8_MFMA && accum != FP8FG_ACCUM_EXACT) return FP8FG_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return -1;  // nothing to do
+  if (K == 0 || K % 128 != 0 || N % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!a || !sa || !b || !sb || !y) return FP8FG_ERR_INVALID_ARG;
+  if (M > kInt32Max || N > kInt32Max || K > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(y, 16) || !aligned(sa, 4) || !aligned(sb, 4))
+    return FP8FG_ERR_MISALIGNED;
+  return FP8FG_OK;
+}
+
+}  // namespace
+
+int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                   int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
+                   int64_t K, fp8fg_stream_t stream) {
+  if (b_scale_mode != FP8FG_B_BLOCK_128x128 && b_scale_mode != FP8FG_B_ROW_1x128)
+    return FP8FG_ERR_INVALID_ARG;
+  const int c = check_gemm_common(a, sa, b, sb, accum, y, y_dtype, M, N, K);
+  if (c < 0) return FP8FG_OK;
+  if (c != FP8FG_OK) return c;
+  // launch grid: ceil(M/128) * (N/128) blocks
+  if (((M + 127) / 128) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  fp8fg::GemmArgs g{a, sa, b, sb, y, nullptr, M, N, K, 1,
+                    b_scale_mode == FP8FG_B_ROW_1x128, accum == FP8FG_ACCUM_EXACT,
+                    y_dtype == FP8FG_BF16};
+  return hip_status(fp8fg::launch_block_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* group_offsets,
+                           int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
+                           int y_dtype, int64_t M_total, int64_t N, int64_t K,
+                           fp8fg_stream_t stream) {
+  if (G < 0) return FP8FG_ERR_INVALID_ARG;
+  const int c = check_gemm_common(a, sa, b, sb, accum, y, y_dtype, M_total, N, K);
+  if (c < 0 || G == 0) return c > 0 ? c : FP8FG_OK;
+  if (c != FP8FG_OK) return c;
+  if (!group_offsets) return FP8FG_ERR_INVALID_ARG;
+  if (!aligned(group_offsets, 4)) return FP8FG_ERR_MISALIGNED;
+  if (G > kInt32Max || (M_total / 128 + G) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  fp8fg::GemmArgs g{a, sa, b, sb, y, group_offsets, M_total, N, K, G,
+                    false, accum == FP8FG_ACCUM_EXACT, y_dtype == FP8FG_BF16};
+  return hip_status(fp8fg::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

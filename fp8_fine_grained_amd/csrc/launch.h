@@ -1,0 +1,35 @@
+// Internal launcher interface between the C-ABI layer (capi.cpp) and the
+// HIP kernels.  Arguments reaching these functions have been validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fp8fg {
+
+// 1x128 quantisation, row-contiguous input (stride_k == 1).
+hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+                                 uint8_t* q, float* scales, hipStream_t s);
+// 1x128 quantisation along K of a column-contiguous input (stride_m == 1):
+// x is physically [K, ld] row-major, element (m, k) at k*ld + m.
+hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+                                 uint8_t* q, float* scales, hipStream_t s);
+// 128x128 quantisation.
+hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+                               uint8_t* q, float* scales, hipStream_t s);
+
+struct GemmArgs {
+  const uint8_t* a;
+  const float* sa;
+  const uint8_t* b;
+  const float* sb;
+  void* y;
+  const int32_t* offsets;  // grouped only
+  int64_t M, N, K, G;
+  bool row_scales;  // B scales per row (1x128) instead of per 128x128 block
+  bool exact;       // exact products (fp16 matrix cores) instead of FP8 MFMA
+  bool y_bf16;
+};
+hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t s);
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
+
+}  // namespace fp8fg

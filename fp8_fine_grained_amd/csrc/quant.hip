@@ -1,0 +1,272 @@
+// Online fine-grained quantisation to OCP E4M3 on gfx950.
+//
+// Per group (1x128 activation tile or 128x128 weight block; Figure 7(a)
+// passage of the innerforce DeepSeek-V3 notes, yunhecapital report section
+// 2.2.3, tonho.wtf "DeepSeek-V3" section "como funciona"):
+//     amax = max|x|,  s = fl32(amax/448),  inv = s ? fl32(1/s) : 0,
+//     q = E4M3 RNE cast of fl32(x*inv), sign kept.
+// The divisions use HIP's correctly rounded fp32 division (no fast math).
+// |x*inv| <= 448*(1+3*2^-24) < 464, so the hardware cvt, which rounds to
+// nearest even and maps [448, 464] to 448, never reaches its NaN range and
+// no explicit clamp is needed; zero groups give inv = 0 and codes 0x00/0x80.
+#include "launch.h"
+
+namespace fp8fg {
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
+  s = amax / kE4M3Max;
+  inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+}
+
+// Four fp32 values -> four E4M3 bytes (little-endian order a, b, c, d).
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return static_cast<uint32_t>(v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+// Max over each aligned group of 8 lanes (quad xor 1, quad xor 2, half-row mirror).
+__device__ __forceinline__ float max8(float v) {
+  v = dpp_max<0xB1>(v);
+  v = dpp_max<0x4E>(v);
+  return dpp_max<0x141>(v);
+}
+// Max over the 64-lane wavefront.
+__device__ __forceinline__ float max64(float v) {
+  v = max8(v);
+  v = dpp_max<0x140>(v);  // row mirror: max over 16
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+// Load 16 consecutive elements starting at p (16-byte aligned) as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* p, float (&v)[16]) {
+  if constexpr (BF16) {
+    const u32x4* u = reinterpret_cast<const u32x4*>(p);
+    u32x4 a = __builtin_nontemporal_load(u);
+    u32x4 b = __builtin_nontemporal_load(u + 1);
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const f32x4* f = reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x4 t = __builtin_nontemporal_load(f + i);
+      v[4 * i] = t.x;
+      v[4 * i + 1] = t.y;
+      v[4 * i + 2] = t.z;
+      v[4 * i + 3] = t.w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 1x128, rows
+// Eight lanes own one 1x128 tile (16 elements each); a 256-thread block
+// covers 32 consecutive tiles of the row-major [M, K/128] tile grid.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restrict__ x, int64_t ld,
+                                                             int G, int64_t tiles,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scales, int64_t K) {
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  const bool live = tile < tiles;
+  const int64_t t = live ? tile : tiles - 1;  // dead lanes mirror the last tile; they store nothing
+  const int64_t m = t / G;
+  const int g = static_cast<int>(t - m * G);
+  const int64_t col = static_cast<int64_t>(g) * 128 + part * 16;
+  constexpr int ES = BF16 ? 2 : 4;
+  const char* src = static_cast<const char*>(x) + (m * ld + col) * ES;
+
+  float v[16];
+  load16<BF16>(src, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = max8(amax);
+  float s, inv;
+  group_scale(amax, s, inv);
+  u32x4 out;
+  out.x = cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  out.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  out.z = cvt4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
+  out.w = cvt4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
+  if (live) {
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(q + m * K + col));
+    if (part == 0) scales[t] = s;
+  }
+}
+
+// ------------------------------------------------------- 1x128, transposed
+// Input physically [K, ld] (e.g. tokens x channels); logical row m is column m.
+// Each lane owns COLS adjacent logical rows (bf16: 2, one dword of each
+// physical row; fp32: 1) over one 128-long group and keeps the 128 raw dwords
+// in registers, so a wavefront reads 64 contiguous dwords of each physical row.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_act_cols_kernel(const void* __restrict__ x, int64_t ld,
+                                                             int64_t M, int G,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scales, int64_t K) {
+  constexpr int COLS = BF16 ? 2 : 1;
+  const int64_t lane_col = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
+  const int g = static_cast<int>(blockIdx.y) * 4 + (threadIdx.x >> 6);
+  const int64_t m0 = lane_col * COLS;
+  if (m0 >= M || g >= G) return;  // no cross-lane operations below
+  const int64_t k0 = static_cast<int64_t>(g) * 128;
+  const int64_t step = ld / COLS;  // dwords per physical row
+  const uint32_t* base = static_cast<const uint32_t*>(x) + (k0 * ld + m0) / COLS;
+  uint32_t w[128];
+#pragma unroll
+  for (int t = 0; t < 128; ++t) w[t] = __builtin_nontemporal_load(base + t * step);
+  auto lo = [](uint32_t u) { return BF16 ? bf16_lo(u) : __uint_as_float(u); };
+  float amax0 = 0.0f, amax1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 128; ++t) {
+    amax0 = fmaxf(amax0, fabsf(lo(w[t])));
+    if constexpr (BF16) amax1 = fmaxf(amax1, fabsf(bf16_hi(w[t])));
+  }
+  float s0, inv0, s1 = 0.0f, inv1 = 0.0f;
+  group_scale(amax0, s0, inv0);
+  if constexpr (BF16) group_scale(amax1, s1, inv1);
+  u32x4* qa = reinterpret_cast<u32x4*>(q + m0 * K + k0);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int t = c * 16;
+    u32x4 o;
+    o.x = cvt4(lo(w[t]) * inv0, lo(w[t + 1]) * inv0, lo(w[t + 2]) * inv0, lo(w[t + 3]) * inv0);
+    o.y = cvt4(lo(w[t + 4]) * inv0, lo(w[t + 5]) * inv0, lo(w[t + 6]) * inv0, lo(w[t + 7]) * inv0);
+    o.z = cvt4(lo(w[t + 8]) * inv0, lo(w[t + 9]) * inv0, lo(w[t + 10]) * inv0, lo(w[t + 11]) * inv0);
+    o.w = cvt4(lo(w[t + 12]) * inv0, lo(w[t + 13]) * inv0, lo(w[t + 14]) * inv0, lo(w[t + 15]) * inv0);
+    __builtin_nontemporal_store(o, qa + c);
+  }
+  scales[m0 * G + g] = s0;
+  if constexpr (BF16) {
+    u32x4* qb = reinterpret_cast<u32x4*>(q + (m0 + 1) * K + k0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int t = c * 16;
+      u32x4 o;
+      o.x = cvt4(bf16_hi(w[t]) * inv1, bf16_hi(w[t + 1]) * inv1, bf16_hi(w[t + 2]) * inv1, bf16_hi(w[t + 3]) * inv1);
+      o.y = cvt4(bf16_hi(w[t + 4]) * inv1, bf16_hi(w[t + 5]) * inv1, bf16_hi(w[t + 6]) * inv1, bf16_hi(w[t + 7]) * inv1);
+      o.z = cvt4(bf16_hi(w[t + 8]) * inv1, bf16_hi(w[t + 9]) * inv1, bf16_hi(w[t + 10]) * inv1, bf16_hi(w[t + 11]) * inv1);
+      o.w = cvt4(bf16_hi(w[t + 12]) * inv1, bf16_hi(w[t + 13]) * inv1, bf16_hi(w[t + 14]) * inv1, bf16_hi(w[t + 15]) * inv1);
+      __builtin_nontemporal_store(o, qb + c);
+    }
+    scales[(m0 + 1) * G + g] = s1;
+  }
+}
+
+// ---------------------------------------------------------------- 128x128
+// One 256-thread block per 128x128 block, read from HBM once: thread t holds
+// columns 8*(t%16) .. +7 of rows t/16 + 16*i (i = 0..7) in registers.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_weight_kernel(const void* __restrict__ w, int64_t ld,
+                                                           int GK, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scales, int64_t K) {
+  __shared__ float wave_max[4];
+  const int bi = blockIdx.x / GK;
+  const int bj = blockIdx.x - bi * GK;
+  const int c8 = (threadIdx.x & 15) * 8;
+  const int r0 = threadIdx.x >> 4;
+  constexpr int ES = BF16 ? 2 : 4;
+  float v[8][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = static_cast<int64_t>(bi) * 128 + r0 + 16 * i;
+    const char* src = static_cast<const char*>(w) + (row * ld + static_cast<int64_t>(bj) * 128 + c8) * ES;
+    if constexpr (BF16) {
+      u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[i][2 * j] = bf16_lo(wd[j]);
+        v[i][2 * j + 1] = bf16_hi(wd[j]);
+      }
+    } else {
+      f32x4 f0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+      f32x4 f1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + 1);
+      v[i][0] = f0.x; v[i][1] = f0.y; v[i][2] = f0.z; v[i][3] = f0.w;
+      v[i][4] = f1.x; v[i][5] = f1.y; v[i][6] = f1.z; v[i][7] = f1.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+  amax = max64(amax);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  float s, inv;
+  group_scale(amax, s, inv);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = static_cast<int64_t>(bi) * 128 + r0 + 16 * i;
+    u32x2 o;
+    o.x = cvt4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+    o.y = cvt4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + row * K + static_cast<int64_t>(bj) * 128 + c8));
+  }
+  if (threadIdx.x == 0) scales[blockIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+                                 uint8_t* q, float* scales, hipStream_t s) {
+  const int G = static_cast<int>(K / 128);
+  const int64_t tiles = M * G;
+  const dim3 grid(static_cast<unsigned>((tiles + 31) / 32));
+  if (bf16)
+    hipLaunchKernelGGL(quant_act_rows_kernel<true>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, K);
+  else
+    hipLaunchKernelGGL(quant_act_rows_kernel<false>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+                                 uint8_t* q, float* scales, hipStream_t s) {
+  const int G = static_cast<int>(K / 128);
+  const int64_t lane_cols = bf16 ? (M + 1) / 2 : M;
+  const dim3 grid(static_cast<unsigned>((lane_cols + 63) / 64), static_cast<unsigned>((G + 3) / 4));
+  if (bf16)
+    hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, s, x, ld, M, G, q, scales, K);
+  else
+    hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(256), 0, s, x, ld, M, G, q, scales, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+                               uint8_t* q, float* scales, hipStream_t s) {
+  const int GK = static_cast<int>(K / 128);
+  const dim3 grid(static_cast<unsigned>((N / 128) * GK));
+  if (bf16)
+    hipLaunchKernelGGL(quant_weight_kernel<true>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
+  else
+    hipLaunchKernelGGL(quant_weight_kernel<false>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
+  return hipGetLastError();
+}
+
+}  // namespace fp8fg

@@ -178,3 +178,24 @@ def skewed_offsets(M_total, G, big_rows, n_empty, seed=7):
     offsets = np.zeros(G + 1, dtype=np.int32)
     offsets[1:] = np.cumsum(counts)
     return offsets
+
+
+def moe_expert_weights(experts, seed=4, N=2048, K=7168):
+    """Stacked bf16 [len(experts), N, K] of the given experts' weights (threaded over experts)."""
+    experts = list(experts)
+    out = torch.empty((len(experts), N, K), dtype=torch.bfloat16)
+
+    def one(i):
+        g = experts[i]
+        rng_rows = []
+        for c, r0 in enumerate(range(0, N, _CHUNK_ROWS)):
+            r1 = min(N, r0 + _CHUNK_ROWS)
+            rng = np.random.default_rng([seed, 100 + int(g), c])
+            v = rng.standard_normal((r1 - r0, K), dtype=np.float32)
+            v *= np.float32(0.02)
+            rng_rows.append(v)
+        out[i] = to_bf16(np.concatenate(rng_rows))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(len(experts))))
+    return out

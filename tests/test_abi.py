@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports every function include/fp8fg.h declares,
+and rejects invalid arguments on the host (no kernel is launched by any call
+here: each one fails validation, or is a documented no-op)."""
+
+import ctypes
+
+import pytest
+
+from fp8_fine_grained_amd import binding as fp8
+
+BAD = ctypes.c_void_p(0x1008)   # 8-byte aligned, not 16: never dereferenced
+GOOD = ctypes.c_void_p(0x10000)  # aligned stand-in: only used where validation fails first
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fp8.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = fp8.declared_functions()
+    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_block_gemm",
+                          "fp8_block_grouped_gemm", "fp8fg_status_string", "fp8fg_abi_version"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8fg_abi_version() == 1
+    for st in range(0, 6):
+        assert L.fp8fg_status_string(st)
+    assert b"unknown" in L.fp8fg_status_string(99)
+
+
+def test_quant_act_validation(L):
+    f = L.fp8_quant_act_1x128
+    assert f(GOOD, 7, 4, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG  # dtype
+    assert f(GOOD, fp8.BF16, -1, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG
+    assert f(NULL, fp8.BF16, 0, 128, 128, 1, NULL, NULL, NULL) == fp8.OK  # M == 0: no-op
+    assert f(GOOD, fp8.BF16, 4, 100, 100, 1, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED
+    assert f(NULL, fp8.BF16, 4, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG
+    assert f(BAD, fp8.BF16, 4, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_MISALIGNED
+    assert f(GOOD, fp8.BF16, 4, 128, 128, 1, BAD, GOOD, NULL) == fp8.ERR_MISALIGNED
+    assert f(GOOD, fp8.BF16, 4, 128, 129, 1, GOOD, GOOD, NULL) == fp8.ERR_MISALIGNED  # row pitch
+    assert f(GOOD, fp8.BF16, 4, 128, 2, 3, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED   # strided both ways
+    assert f(GOOD, fp8.BF16, 12, 128, 1, 16, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED  # transposed, M % 8
+
+
+def test_quant_weight_validation(L):
+    f = L.fp8_quant_weight_128x128
+    assert f(GOOD, fp8.BF16, 100, 128, 128, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED
+    assert f(GOOD, fp8.BF16, 128, 130, 130, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED
+    assert f(GOOD, fp8.BF16, 128, 128, 64, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG  # ld < K
+    assert f(GOOD, fp8.F32, 128, 128, 128, NULL, GOOD, NULL) == fp8.ERR_INVALID_ARG
+    assert f(GOOD, fp8.F32, 128, 128, 128, GOOD, ctypes.c_void_p(0x10002), NULL) == fp8.ERR_MISALIGNED
+    assert f(NULL, fp8.F32, 0, 128, 128, NULL, NULL, NULL) == fp8.OK
+
+
+def test_gemm_validation(L):
+    f = L.fp8_block_gemm
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("a", GOOD), ("sa", GOOD), ("b", GOOD), ("sb", GOOD), ("mode", fp8.B_BLOCK_128x128),
+        ("accum", fp8.ACCUM_FP8_MFMA), ("y", GOOD), ("ydt", fp8.BF16), ("M", 4), ("N", 128),
+        ("K", 256), ("s", NULL))]
+    assert f(*args(mode=5)) == fp8.ERR_INVALID_ARG
+    assert f(*args(accum=9)) == fp8.ERR_INVALID_ARG
+    assert f(*args(ydt=3)) == fp8.ERR_INVALID_ARG
+    assert f(*args(M=-2)) == fp8.ERR_INVALID_ARG
+    assert f(*args(a=NULL, M=0)) == fp8.OK
+    assert f(*args(K=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(N=100)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(K=0)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(sb=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(y=BAD)) == fp8.ERR_MISALIGNED
+    assert f(*args(sa=ctypes.c_void_p(0x10001))) == fp8.ERR_MISALIGNED
+
+
+def test_grouped_validation(L):
+    f = L.fp8_block_grouped_gemm
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("a", GOOD), ("sa", GOOD), ("off", GOOD), ("G", 4), ("b", GOOD), ("sb", GOOD),
+        ("accum", fp8.ACCUM_FP8_MFMA), ("y", GOOD), ("ydt", fp8.BF16), ("M", 64), ("N", 128),
+        ("K", 256), ("s", NULL))]
+    assert f(*args(G=-1)) == fp8.ERR_INVALID_ARG
+    assert f(*args(off=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(off=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(N=192)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(G=0)) == fp8.OK
+    assert f(*args(M=0, a=NULL)) == fp8.OK

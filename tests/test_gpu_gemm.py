@@ -1,0 +1,132 @@
+"""GPU parity of the block-scaled GEMM against the fp64 oracle.
+
+bf16 outputs: |y - ref| <= half a bf16 ulp of ref + 8e-3 * rms(ref) per element.
+fp32 outputs with exact accumulation: Frobenius relative error <= 1e-5.
+fp32 outputs with FP8 matrix-core accumulation: per-element bound derived from
+the hardware's measured in-group truncation (tests.gpu_util.fp8_mfma_bound).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_amd import binding as fp8, workloads
+from oracle import gemm, quant
+from tests.gpu_util import check_bf16, check_f32, check_guard, f32, fp8_mfma_bound, frob_rel, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantised(x_cpu, w_cpu):
+    """(GPU operands from the HIP quantisers, oracle operands from the oracle quantisers)."""
+    qa, sa = fp8.fp8_quant_act_1x128(x_cpu.cuda())
+    qb, sb = fp8.fp8_quant_weight_128x128(w_cpu.cuda())
+    ra, rsa = quant.quant_1x128(f32(x_cpu))
+    rb, rsb = quant.quant_128x128(f32(w_cpu))
+    assert np.array_equal(qa.cpu().numpy(), ra) and np.array_equal(qb.cpu().numpy(), rb)
+    return (qa, sa, qb, sb), (ra, rsa, rb, rsb)
+
+
+def _run(gpu_ops, M, N, out_dtype, accum, mode="block"):
+    qa, sa, qb, sb = gpu_ops
+    buf, y = guarded((M, N), out_dtype)
+    fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode=mode, accum=accum, y=y)
+    torch.cuda.synchronize()
+    check_guard(buf)
+    return y
+
+
+def test_tiny_fp32_exact_and_fp8():
+    t = workloads.tiny()
+    g, r = _quantised(t["x"], t["w"])
+    ref = gemm.block_gemm(*r)
+    say("tiny 128x128x256")
+    check_f32(_run(g, 128, 128, torch.float32, "exact"), ref, "exact accumulation")
+    y8 = f32(_run(g, 128, 128, torch.float32, "fp8")).astype(np.float64)
+    bound = fp8_mfma_bound(*r, "block")
+    say(f"  fp8 accumulation: Frobenius {frob_rel(y8, ref):.3e}, max err/bound {np.max(np.abs(y8 - ref) / bound):.3f}")
+    assert np.all(np.abs(y8 - ref) <= bound)
+    check_bf16(_run(g, 128, 128, torch.bfloat16, "fp8"), ref, "bf16 out")
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (1, 128, 128), (129, 256, 384), (64, 128, 7168)])
+def test_dense_shapes_bf16(M, N, K):
+    d = workloads.dense(M=M, N=N, K=K)
+    g, r = _quantised(d["x"], d["w"])
+    ref = gemm.block_gemm(*r)
+    say(f"dense {M}x{N}x{K}")
+    check_bf16(_run(g, M, N, torch.bfloat16, "fp8"), ref, "fp8 accum")
+    check_bf16(_run(g, M, N, torch.bfloat16, "exact"), ref, "exact accum")
+    check_f32(_run(g, M, N, torch.float32, "exact"), ref, "exact accum fp32")
+
+
+def test_zero_rows_give_zero():
+    d = workloads.dense(M=130, N=256, K=512)
+    x = d["x"].clone()
+    x[5] = 0
+    x[129, :256] = 0
+    g, r = _quantised(x, d["w"])
+    y = f32(_run(g, 130, 256, torch.float32, "fp8"))
+    assert np.all(y[5] == 0)
+    ref = gemm.block_gemm(*r)
+    check_f32(f32(_run(g, 130, 256, torch.float32, "exact")).astype(np.float64), ref, "with zero tiles")
+
+
+def _wgrad_ops(T, Cout, Cin):
+    d = workloads.wgrad(T=T, C=Cout, Cin=Cin)
+    qa, sa = fp8.fp8_quant_act_1x128(d["dy"].cuda().t())
+    qb, sb = fp8.fp8_quant_act_1x128(d["x"].cuda().t())
+    ra, rsa = quant.quant_1x128_along_rows(f32(d["dy"]))
+    rb, rsb = quant.quant_1x128_along_rows(f32(d["x"]))
+    assert np.array_equal(qa.cpu().numpy(), ra) and np.array_equal(qb.cpu().numpy(), rb)
+    return (qa, sa, qb, sb), (ra, rsa, rb, rsb)
+
+
+def test_wgrad_row_scales_small():
+    g, r = _wgrad_ops(640, 200, 256)
+    ref = gemm.block_gemm(*r, mode="row")
+    say("wgrad 200x256x640 (row-scaled B)")
+    check_f32(_run(g, 200, 256, torch.float32, "exact", "row"), ref, "exact accumulation")
+    y8 = f32(_run(g, 200, 256, torch.float32, "fp8", "row")).astype(np.float64)
+    bound = fp8_mfma_bound(*r, "row")
+    say(f"  fp8 accumulation: Frobenius {frob_rel(y8, ref):.3e}, max err/bound {np.max(np.abs(y8 - ref) / bound):.3f}")
+    assert np.all(np.abs(y8 - ref) <= bound)
+
+
+def _sample_rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], rng.choice(M, size=n, replace=False)]))
+    return rows
+
+
+def test_full_dense_projection():
+    d = workloads.dense()
+    say("dense 4096x7168x7168: quantise + GEMM on GPU")
+    qa, sa = fp8.fp8_quant_act_1x128(d["x"].cuda())
+    qb, sb = fp8.fp8_quant_weight_128x128(d["w"].cuda())
+    y = fp8.fp8_block_gemm(qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    rows = _sample_rows(4096, 60, 1)
+    ra, rsa = quant.quant_1x128(f32(d["x"][rows]))
+    rb, rsb = quant.quant_128x128(f32(d["w"]))
+    assert np.array_equal(qb.cpu().numpy(), rb)
+    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    ref = gemm.block_gemm(ra, rsa, rb, rsb)
+    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows")
+    assert torch.isfinite(y.float()).all()
+
+
+def test_full_wgrad():
+    d = workloads.wgrad()
+    say("wgrad 7168x7168x16384: transposed quantisation + row-scaled GEMM on GPU")
+    qa, sa = fp8.fp8_quant_act_1x128(d["dy"].cuda().t())
+    qb, sb = fp8.fp8_quant_act_1x128(d["x"].cuda().t())
+    y = fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = _sample_rows(7168, 12, 2)
+    rb, rsb = quant.quant_1x128_along_rows(f32(d["x"]))
+    assert np.array_equal(qb.cpu().numpy(), rb)
+    ra, rsa = quant.quant_1x128_along_rows(f32(d["dy"][:, rows]))
+    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    ref = gemm.block_gemm(ra, rsa, rb, rsb, mode="row")
+    check_f32(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows, exact accumulation")

@@ -1,0 +1,115 @@
+"""GPU parity of the grouped (mixture-of-experts) block-scaled GEMM."""
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_amd import binding as fp8, workloads
+from oracle import gemm, quant
+from tests.gpu_util import check_bf16, check_f32, check_guard, f32, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(offsets, N, K, seed):
+    offsets = np.asarray(offsets, dtype=np.int32)
+    G = offsets.size - 1
+    M = int(offsets[-1])
+    x = workloads.dense(seed=seed, M=max(M, 1), N=128, K=K)["x"][:M]
+    w = torch.stack([workloads.moe_expert_weight(g, seed=seed, N=N, K=K) for g in range(G)])
+    qa, sa = fp8.fp8_quant_act_1x128(x.cuda()) if M else (torch.empty((0, K), dtype=torch.uint8, device="cuda"),
+                                                          torch.empty((0, K // 128), device="cuda"))
+    qb, sb = fp8.fp8_quant_weight_128x128(w.cuda().view(G * N, K))
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    ra, rsa = quant.quant_1x128(f32(x)) if M else (np.zeros((0, K), np.uint8), np.zeros((0, K // 128), np.float32))
+    rb = np.empty((G, N, K), np.uint8)
+    rsb = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        rb[g], rsb[g] = quant.quant_128x128(f32(w[g]))
+    assert np.array_equal(qb.cpu().numpy(), rb)
+    off = torch.from_numpy(offsets).cuda()
+    return (qa, sa, off, qb, sb), (ra, rsa, offsets, rb, rsb)
+
+
+def _run(g, M, N, dtype, accum):
+    buf, y = guarded((M, N), dtype)
+    fp8.fp8_block_grouped_gemm(*g, accum=accum, y=y)
+    torch.cuda.synchronize()
+    check_guard(buf)
+    return y
+
+
+def test_small_ragged_segments():
+    sizes = [5, 0, 1, 300, 0, 17, 129, 128]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    g, r = _case(off, 256, 512, 11)
+    ref = gemm.grouped_gemm(*r)
+    say(f"grouped sizes {sizes}, N=256, K=512")
+    check_bf16(_run(g, int(off[-1]), 256, torch.bfloat16, "fp8"), ref, "fp8 accum")
+    check_f32(_run(g, int(off[-1]), 256, torch.float32, "exact"), ref, "exact accum fp32")
+
+
+def test_skewed_routing():
+    off = workloads.skewed_offsets(3000, 32, 1500, 6)
+    g, r = _case(off, 128, 256, 12)
+    ref = gemm.grouped_gemm(*r)
+    say("grouped skewed: one expert 1500 rows, 6 empty")
+    check_bf16(_run(g, 3000, 128, torch.bfloat16, "fp8"), ref, "fp8 accum")
+
+
+def test_single_group_matches_dense_kernel():
+    off = np.array([0, 333])
+    g, r = _case(off, 256, 384, 13)
+    yg = _run(g, 333, 256, torch.float32, "fp8")
+    qa, sa, _, qb, sb = g
+    yd = fp8.fp8_block_gemm(qa, sa, qb[0].contiguous(), sb[0].contiguous(), accum="fp8", out_dtype=torch.float32)
+    assert torch.equal(yg, yd)
+
+
+def test_empty_inputs_are_noops():
+    K, N = 256, 128
+    a = torch.empty((0, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((0, 2), device="cuda")
+    b = torch.zeros((2, N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.zeros((2, 1, 2), device="cuda")
+    off = torch.zeros(3, dtype=torch.int32, device="cuda")
+    y = fp8.fp8_block_grouped_gemm(a, sa, off, b, sb)
+    assert y.shape == (0, N)
+
+
+def test_full_moe_up_projection():
+    say("MoE up-projection: 8192 tokens, 256 experts top-8, W [2048,7168] per expert")
+    route = workloads.moe_routing()
+    tokens = workloads.moe_tokens()
+    perm = torch.from_numpy(route["perm"])
+    offsets = route["offsets"]
+    say("  generating expert weights")
+    w = workloads.moe_expert_weights(range(256))
+    say("  quantise + grouped GEMM on GPU")
+    xa = tokens.cuda()[perm.cuda()]
+    qa, sa = fp8.fp8_quant_act_1x128(xa)
+    wd = w.cuda()
+    qb, sb = fp8.fp8_quant_weight_128x128(wd.view(256 * 2048, 7168))
+    del wd
+    qb, sb = qb.view(256, 2048, 7168), sb.view(256, 16, 56)
+    y = fp8.fp8_block_grouped_gemm(qa, sa, torch.from_numpy(offsets).cuda(), qb, sb)
+    torch.cuda.synchronize()
+    sizes = np.diff(offsets)
+    rng = np.random.default_rng(3)
+    experts = sorted({0, 255, int(np.argmax(sizes)), int(np.argmin(sizes)), *rng.choice(256, 6, replace=False).tolist()})
+    rows = []
+    for e in experts:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows += [lo, hi - 1, int(rng.integers(lo, hi))]
+    rows = np.array(sorted(set(rows)))
+    say(f"  oracle on experts {experts}, {rows.size} rows")
+    ra, rsa = quant.quant_1x128(f32(tokens[perm[rows]]))
+    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    ref = np.zeros((rows.size, 2048))
+    expert_of = np.searchsorted(offsets, rows, side="right") - 1
+    for e in experts:
+        qe, se = quant.quant_128x128(f32(w[e]))
+        assert np.array_equal(qb[e].cpu().numpy(), qe)
+        sel = np.nonzero(expert_of == e)[0]
+        ref[sel] = gemm.block_gemm(ra[sel], rsa[sel], qe, se)
+    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows")

@@ -1,0 +1,174 @@
+"""GPU parity of the quantisers against the oracle: codes and scales bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_amd import binding as fp8, workloads
+from oracle import e4m3, quant
+from tests.gpu_util import assert_codes_equal, assert_scales_equal, check_guard, f32, guarded, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _act_rows(x_cpu, what):
+    say(f"quant_act rows {what} {tuple(x_cpu.shape)} {x_cpu.dtype}")
+    M, K = x_cpu.shape
+    x = x_cpu.cuda()
+    qb, q = guarded((M, K), torch.uint8)
+    sbuf, s = guarded((M, K // 128), torch.float32)
+    fp8.fp8_quant_act_1x128(x, q, s)
+    torch.cuda.synchronize()
+    check_guard(qb)
+    check_guard(sbuf)
+    q_ref, s_ref = quant.quant_1x128(f32(x_cpu))
+    assert_codes_equal(q, q_ref, what)
+    assert_scales_equal(s, s_ref, what)
+    return q, s
+
+
+def _special_tiles():
+    """Rows built to hit the corners of the cast: zero and -0 tiles, exact E4M3
+    tiles, ties, power-of-two scaled copies, subnormal-range values."""
+    rng = np.random.default_rng(99)
+    rows = []
+    z = np.zeros(1024, np.float32)
+    rows.append(z.copy())
+    nz = z.copy()
+    nz[::3] = -0.0
+    rows.append(nz)
+    codes = rng.integers(0, 256, size=1024).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A
+    codes[::128] = 0x7E
+    rows.append(e4m3.DECODE_TABLE[codes].astype(np.float32))
+    base = rng.standard_normal(1024).astype(np.float32)
+    for j in (-30, -8, 0, 7, 40):
+        rows.append(base * np.float32(2.0 ** j))
+    tiny_range = base.copy()
+    tiny_range[::2] *= np.float32(1e-4)  # many elements fall to E4M3 subnormals / zero
+    rows.append(tiny_range)
+    ties = np.zeros(1024, np.float32)
+    ties[::128] = 896.0  # scale 2: grid midpoints below map to exact ties
+    mids = (e4m3.DECODE_TABLE[:0x7E] + e4m3.DECODE_TABLE[1:0x7F]) / 2
+    for g in range(8):
+        ties[g * 128 + 1: g * 128 + 126] = (2 * mids[g * 16: g * 16 + 125] if g * 16 + 125 <= mids.size
+                                            else 2 * np.resize(mids, 125)).astype(np.float32)
+    rows.append(ties)
+    rows.append(-ties)
+    for j in (-1, 3, 12, -60, 90):  # pad to 16 rows (the transposed path needs M % 8 == 0)
+        rows.append(rng.standard_t(2.5, size=1024).astype(np.float32) * np.float32(2.0 ** j))
+    return np.stack(rows)
+
+
+def test_act_rows_tiny_fp32():
+    _act_rows(workloads.tiny()["x"], "tiny fp32")
+
+
+def test_act_rows_ragged_bf16():
+    _act_rows(workloads.dense(M=300, N=128, K=1024)["x"], "dense-like ragged")
+
+
+def test_act_rows_student_t():
+    _act_rows(workloads.quant_act(M=517, K=7168), "student-t")
+
+
+def test_act_rows_special_tiles_fp32_and_bf16():
+    x = _special_tiles()
+    _act_rows(torch.from_numpy(x), "special fp32")
+    _act_rows(workloads.to_bf16(x), "special bf16")
+
+
+def test_act_rows_single_row_and_padded_pitch():
+    x = workloads.dense(M=1, N=128, K=256)["x"]
+    _act_rows(x, "M=1")
+    big = workloads.dense(M=40, N=128, K=512)["x"]
+    view = big[:, :384]  # pitch 512 elements, logical K 384
+    say("quant_act rows with pitch > K")
+    q, s = fp8.fp8_quant_act_1x128(big.cuda()[:, :384])
+    q_ref, s_ref = quant.quant_1x128(f32(view))
+    assert_codes_equal(q, q_ref, "pitch")
+    assert_scales_equal(s, s_ref, "pitch")
+
+
+def test_act_rows_deterministic():
+    x = workloads.quant_act(M=256, K=2048).cuda()
+    q1, s1 = fp8.fp8_quant_act_1x128(x)
+    q2, s2 = fp8.fp8_quant_act_1x128(x)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def _act_cols(x_phys_cpu, what):
+    """x_phys [T, C]: quantise along T (the gradient-operand layout)."""
+    say(f"quant_act transposed {what} {tuple(x_phys_cpu.shape)}")
+    T, C = x_phys_cpu.shape
+    x = x_phys_cpu.cuda()
+    qb, q = guarded((C, T), torch.uint8)
+    sbuf, s = guarded((C, T // 128), torch.float32)
+    fp8.fp8_quant_act_1x128(x.t(), q, s)
+    torch.cuda.synchronize()
+    check_guard(qb)
+    check_guard(sbuf)
+    q_ref, s_ref = quant.quant_1x128_along_rows(f32(x_phys_cpu))
+    assert_codes_equal(q, q_ref, what)
+    assert_scales_equal(s, s_ref, what)
+    return q, s
+
+
+def test_act_cols_small():
+    d = workloads.wgrad(T=384, C=200, Cin=136)
+    _act_cols(d["dy"], "dY")
+    _act_cols(d["x"], "X")
+    _act_cols(torch.from_numpy(_special_tiles().T.copy()), "special fp32")
+
+
+def test_weight_small():
+    for w, what in ((workloads.tiny()["w"], "tiny fp32"),
+                    (workloads.dense(M=1, N=384, K=1024)["w"], "dense-like bf16"),
+                    (torch.from_numpy(_special_tiles()[:8].reshape(8, 1024)[:, :].repeat(16, axis=0)[:128]), "special")):
+        say(f"quant_weight {what} {tuple(w.shape)}")
+        N, K = w.shape
+        qb, q = guarded((N, K), torch.uint8)
+        sbuf, s = guarded((N // 128, K // 128), torch.float32)
+        fp8.fp8_quant_weight_128x128(w.cuda(), q, s)
+        torch.cuda.synchronize()
+        check_guard(qb)
+        check_guard(sbuf)
+        q_ref, s_ref = quant.quant_128x128(f32(w))
+        assert_codes_equal(q, q_ref, what)
+        assert_scales_equal(s, s_ref, what)
+
+
+def test_validation_errors_reported():
+    x = torch.zeros((4, 100), device="cuda")
+    with pytest.raises(fp8.Fp8fgError) as e:
+        fp8.fp8_quant_act_1x128(x)
+    assert e.value.status == fp8.ERR_UNSUPPORTED
+    w = torch.zeros((100, 128), device="cuda")
+    with pytest.raises(fp8.Fp8fgError) as e:
+        fp8.fp8_quant_weight_128x128(w)
+    assert e.value.status == fp8.ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ full sizes
+
+def test_full_dense_activation():
+    _act_rows(workloads.dense()["x"], "dense X [4096,7168]")
+
+
+def test_full_quant_act():
+    _act_rows(workloads.quant_act(), "act [16384,7168]")
+
+
+def test_full_quant_weight():
+    w = workloads.quant_weight()
+    say("quant_weight full [7168,18432]")
+    q, s = fp8.fp8_quant_weight_128x128(w.cuda())
+    q_ref, s_ref = quant.quant_128x128(f32(w))
+    assert_codes_equal(q, q_ref, "weight full")
+    assert_scales_equal(s, s_ref, "weight full")
+
+
+def test_full_wgrad_operands():
+    d = workloads.wgrad()
+    _act_cols(d["dy"], "dY [16384,7168]")
+    _act_cols(d["x"], "X [16384,7168]")
