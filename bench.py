@@ -1,0 +1,396 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 fine-grained quantisation + block-scaled GEMM path on one MI355X.
+
+Default workload (one "step" = the whole hot path on one batch, inputs resident
+in HBM): the dense projection  X bf16 [4096,7168] (N(0,1), 0.1% x100 outliers),
+W bf16 [7168,7168] (N(0,0.02)):
+    fp8_quant_act_1x128(X) -> fp8_quant_weight_128x128(W) -> fp8_block_gemm -> Y bf16
+The metric is GEMM TFLOP/s of the whole step (2*M*N*K / step time); each
+kernel is also timed with HIP events on the stream it runs on.  The three
+inputs are rotated over three HBM copies so that the 256 MB last-level cache
+cannot serve the quantisers' reads from one step to the next.
+
+Other workloads (``--workload quant|moe|wgrad``) measure the remaining rows of
+the path and print their own JSON line; the default run prints exactly one line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad]
+                    [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 matrix-core peak
+PEAK_FP16_TFLOPS = 2500.0  # dense fp16/bf16 matrix-core peak (exact accumulation path)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(record_name, kernel_src, launches_bytes_key="per_launch_bytes"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
+
+    The summary records the sha256 of the kernel source it was taken with; if
+    the source has changed since, the figure no longer applies and None is
+    returned."""
+    path = os.path.join(ROOT, "profiles", record_name)
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_source_sha256") != _sha(kernel_src):
+        return None
+    return rec.get(launches_bytes_key)
+
+
+class Timer:
+    """HIP-event timing of one kernel launch site on torch's current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        s = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        self.pairs.append([s, None])
+        return self
+
+    def __exit__(self, *a):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        ts = [s.elapsed_time(e) for s, e in self.pairs]
+        return sum(ts) / len(ts) if ts else float("nan")
+
+    def reset(self):
+        self.pairs = []
+
+
+def _cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        n = 1
+    return int(n)
+
+
+# ------------------------------------------------------------------ dense
+
+def bench_dense(args, torch, fp8, workloads):
+    M, N, K = 4096, 7168, 7168
+    d = workloads.dense()
+    xs = [d["x"].cuda() for _ in range(3)]
+    ws = [d["w"].cuda() for _ in range(3)]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    t_act, t_w, t_gemm = Timer(torch), Timer(torch), Timer(torch)
+
+    def step(i, timed):
+        x, w = xs[i % 3], ws[i % 3]
+        if timed:
+            with t_act:
+                fp8.fp8_quant_act_1x128(x, qa, sa)
+            with t_w:
+                fp8.fp8_quant_weight_128x128(w, qb, sb)
+            with t_gemm:
+                fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
+        else:
+            fp8.fp8_quant_act_1x128(x, qa, sa)
+            fp8.fp8_quant_weight_128x128(w, qb, sb)
+            fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    flop = 2.0 * M * N * K
+    gemm_ms = t_gemm.mean_ms()
+    act_ms, w_ms = t_act.mean_ms(), t_w.mean_ms()
+    act_bytes = M * K * (2 + 1) + M * (K // 128) * 4
+    w_bytes = N * K * (2 + 1) + (N // 128) * (K // 128) * 4
+    gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
+    traffic = _traffic("block_gemm_dense_4096x7168x7168_traffic.json",
+                       os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm.hip"))
+    out = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s (% dense FP8 peak); quantizer GB/s (% HBM peak)",
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense projection: quantise X bf16 [4096,7168] per 1x128 and W bf16 [7168,7168] "
+                        "per 128x128 to E4M3, then block-scaled FP8 GEMM Y = X W^T, bf16 out, "
+                        "FP8 matrix-core accumulation promoted to fp32 every 128 K",
+            "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": 3,
+        },
+        "kernels": {
+            "fp8_quant_act_1x128": {"ms": act_ms, "GB/s": act_bytes / (act_ms * 1e-3) / 1e9,
+                                    "frac_hbm": act_bytes / (act_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "fp8_quant_weight_128x128": {"ms": w_ms, "GB/s": w_bytes / (w_ms * 1e-3) / 1e9,
+                                         "frac_hbm": w_bytes / (w_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "fp8_block_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
+                               "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": gemm_tflops,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gemm_tflops / PEAK_FP8_TFLOPS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_dense(d)
+    return out
+
+
+def cpu_baseline_dense(d):
+    """The oracle on a bounded sample of the dense step: 256 rows of X, all of W."""
+    import numpy as np
+
+    from oracle import gemm, quant
+
+    rows = 256
+    x = d["x"][:rows].float().numpy()
+    w = d["w"].float().numpy()
+    t0 = time.perf_counter()
+    ra, rsa = quant.quant_1x128(x)
+    rb, rsb = quant.quant_128x128(w)
+    gemm.block_gemm(ra, rsa, rb, rsb)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * w.shape[0] * w.shape[1]
+    del np
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
+            "sample": f"dense step on X rows 0..{rows - 1} of [4096,7168] with the full W [7168,7168]: "
+                      f"numpy 1x128 + 128x128 quantisation and fp64 GEMM; {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ other rows
+
+def _hbm_line(name, ms, nbytes, extra):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": nbytes, **extra}
+
+
+def bench_quant(args, torch, fp8, workloads):
+    act = workloads.quant_act()
+    w = workloads.quant_weight()
+    acts = [act.cuda() for _ in range(3)]
+    ws = [w.cuda() for _ in range(3)]
+    M, K = act.shape
+    N, KW = w.shape
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qw = torch.empty((N, KW), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((N // 128, KW // 128), dtype=torch.float32, device="cuda")
+    ta, tw = Timer(torch), Timer(torch)
+    for i in range(args.warmup):
+        fp8.fp8_quant_act_1x128(acts[i % 3], qa, sa)
+        fp8.fp8_quant_weight_128x128(ws[i % 3], qw, sw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with ta:
+            fp8.fp8_quant_act_1x128(acts[i % 3], qa, sa)
+        with tw:
+            fp8.fp8_quant_weight_128x128(ws[i % 3], qw, sw)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    ab = M * K * 3 + M * (K // 128) * 4
+    wb = N * KW * 3 + (N // 128) * (KW // 128) * 4
+    act_line = _hbm_line("act", ta.mean_ms(), ab, {})
+    w_line = _hbm_line("weight", tw.mean_ms(), wb, {})
+    return {
+        "metric": "quantizer GB/s (% HBM peak)", "value": (ab + wb) / dt / 1e9, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "quantiser bandwidth: activation bf16 [16384,7168] Student-t nu=3 per 1x128; "
+                               "weight bf16 [7168,18432] N(0,0.02) per 128x128", "input_copies_rotated": 3},
+        "kernels": {"fp8_quant_act_1x128": act_line, "fp8_quant_weight_128x128": w_line},
+        "roofline": {"bound": "hbm", "achieved": act_line["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": act_line["frac_hbm"],
+                     "traffic": _traffic("quant_act_1x128_16384x7168_traffic.json",
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "quant.hip"))},
+    }
+
+
+def bench_moe(args, torch, fp8, workloads):
+    route = workloads.moe_routing()
+    tokens = workloads.moe_tokens()
+    offsets = torch.from_numpy(route["offsets"]).cuda()
+    xa = tokens.cuda()[torch.from_numpy(route["perm"]).cuda()]
+    G, N, K = 256, 2048, 7168
+    Mt = xa.shape[0]
+    # Weights drawn on the GPU from a seeded generator: the benchmark needs no
+    # oracle comparison, and 3.76e9 CPU draws would dominate the run time.
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    w = (torch.randn((G * N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    qb, sb = fp8.fp8_quant_weight_128x128(w)
+    del w
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    qa = torch.empty((Mt, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((Mt, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
+    tq, tg = Timer(torch), Timer(torch)
+    for _ in range(args.warmup):
+        fp8.fp8_quant_act_1x128(xa, qa, sa)
+        fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        with tq:
+            fp8.fp8_quant_act_1x128(xa, qa, sa)
+        with tg:
+            fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    flop = 2.0 * Mt * N * K
+    gms = tg.mean_ms()
+    gemm_bytes = Mt * K + Mt * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4 + Mt * N * 2
+    return {
+        "metric": "grouped FP8 GEMM TFLOP/s", "value": flop / dt / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "MoE up-projection: 8192 tokens x 7168, 256 experts top-8 -> 65536 rows; "
+                               "per-expert W [2048,7168]; 1x128 quant of the dispatched rows + grouped GEMM, bf16 out",
+                   "M_total": Mt, "N": N, "K": K, "G": G},
+        "kernels": {
+            "fp8_quant_act_1x128": _hbm_line("act", tq.mean_ms(), Mt * K * 3 + Mt * (K // 128) * 4, {}),
+            "fp8_block_grouped_gemm": {"ms": gms, "TFLOP/s": flop / (gms * 1e-3) / 1e12,
+                                       "frac_fp8_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                                       "GB/s": gemm_bytes / (gms * 1e-3) / 1e9,
+                                       "frac_hbm": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        },
+        "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": _traffic("grouped_gemm_moe_65536x2048x7168_traffic.json",
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm.hip"))},
+    }
+
+
+def bench_wgrad(args, torch, fp8, workloads):
+    d = workloads.wgrad()
+    dy, x = d["dy"].cuda(), d["x"].cuda()
+    C, T = 7168, 16384
+    qa = torch.empty((C, T), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((C, T // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((C, T), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((C, T // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((C, C), dtype=torch.float32, device="cuda")
+    tq, tg, tf = Timer(torch), Timer(torch), Timer(torch)
+    for _ in range(args.warmup):
+        fp8.fp8_quant_act_1x128(dy.t(), qa, sa)
+        fp8.fp8_quant_act_1x128(x.t(), qb, sb)
+        fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", accum="exact", y=y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        with tq:
+            fp8.fp8_quant_act_1x128(dy.t(), qa, sa)
+            fp8.fp8_quant_act_1x128(x.t(), qb, sb)
+        with tg:
+            fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", accum="exact", y=y)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    for _ in range(max(1, args.steps // 2)):
+        with tf:
+            fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", accum="fp8", y=y)
+    torch.cuda.synchronize()
+    flop = 2.0 * C * C * T
+    gms, fms = tg.mean_ms(), tf.mean_ms()
+    qbytes = 2 * (T * C * 3 + C * (T // 128) * 4)
+    return {
+        "metric": "weight-gradient FP8 GEMM TFLOP/s", "value": flop / dt / 1e12, "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "weight gradient dW = dY^T X: dY, X bf16 [16384,7168] quantised 1x128 along "
+                               "tokens (transposed read), row-scaled GEMM, fp32 out, exact accumulation",
+                   "M": C, "N": C, "K": T},
+        "kernels": {
+            "fp8_quant_act_1x128 (transposed, x2)": _hbm_line("q", tq.mean_ms(), qbytes, {}),
+            "fp8_block_gemm (row scales, exact)": {"ms": gms, "TFLOP/s": flop / (gms * 1e-3) / 1e12,
+                                                   "frac_fp16_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS},
+            "fp8_block_gemm (row scales, fp8 accum)": {"ms": fms, "TFLOP/s": flop / (fms * 1e-3) / 1e12,
+                                                       "frac_fp8_peak": flop / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
+        },
+        "roofline": {"bound": "mfma", "achieved": flop / (gms * 1e-3) / 1e12, "peak": PEAK_FP16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, "traffic": None},
+    }
+
+
+def copy_calibration(args, torch):
+    """A plain 1 GiB device-to-device copy: the reference for scaling rocprofv3 byte counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this "
+              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args, torch)
+        return
+    import fp8_fine_grained_amd.binding as fp8
+    from fp8_fine_grained_amd import workloads
+
+    fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad}[args.workload]
+    out = fn(args, torch, fp8, workloads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfp8fg.so")
-SOURCES = ["quant.hip", "gemm.hip", "capi.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "gemm_fp8.hip", "capi.cpp"]
 ARCH = os.environ.get("FP8FG_ARCH", "gfx950")
 
 FLAGS = [

@@ -332,12 +332,14 @@ hipError_t dispatch(const GemmArgs& g, unsigned blocks, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t s) {
+  if (fp8_block_kernel_applies(g)) return launch_fp8_block_gemm(g, false, s);
   const int64_t mt = (g.M + kBM - 1) / kBM;
   const int64_t nt = g.N / kBN;
   return dispatch<false>(g, static_cast<unsigned>(mt * nt), s);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s) {
+  if (fp8_block_kernel_applies(g)) return launch_fp8_block_gemm(g, true, s);
   // Upper bound on m-tiles: sum_g ceil(rows_g / BM) <= M_total / BM + G.
   const int64_t mt = g.M / kBM + g.G;
   const int64_t nt = g.N / kBN;

@@ -32,4 +32,8 @@ struct GemmArgs {
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
 
+// 256x256-tile FP8-accumulation kernel for 128x128 weight scales (gemm_fp8.hip).
+bool fp8_block_kernel_applies(const GemmArgs& g);
+hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s);
+
 }  // namespace fp8fg
