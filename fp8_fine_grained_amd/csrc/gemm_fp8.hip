@@ -7,12 +7,17 @@
 // section 2.2.3; tonho.wtf "DeepSeek-V3", "como funciona").
 //
 // Layout on gfx950:
-//  * 256 x 256 output tile per 512-thread workgroup: 8 wavefronts (2 per SIMD)
-//    arranged 2 (n) x 4 (m), each 128 (n) x 64 (m) = 8 x 4 sub-tiles of 16 x 16.
-//    At this size the L2 -> CU traffic (64 KB per 16.8 MFLOP) stays within what
-//    the L2 delivers to 256 CUs while the matrix cores run at full rate.
-//  * One 128-wide K block per LDS stage (64 KB), two stages: the loads of block
-//    kb+1 are issued while block kb is multiplied.
+//  * 512-thread workgroups (8 wavefronts, 2 per SIMD), each wavefront owning a
+//    (TN x TM) block of 16 x 16 sub-tiles.  Two tile shapes:
+//      dense   256 (m) x 256 (n), wavefronts 4 (m) x 2 (n) of 64 x 128, 2 stages;
+//      grouped 128 (m) x 256 (n), wavefronts 2 (m) x 4 (n) of 64 x 64, 3 stages
+//    (128-row tiles waste less of the last tile of each ~256-row expert segment).
+//    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
+//  * One 128-wide K block per LDS stage; the loads of block kb+STAGES-1 are in
+//    flight while block kb is multiplied, spread over the sub-tile steps (about
+//    one DMA per step) so the address unit drains while the matrix cores run.
+//    One further block is only touched: one 4-byte DMA per 128-byte line (into a
+//    scratch LDS slot nobody reads) pulls it into L2 ahead of its real loads.
 //  * Tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    issued through inline assembly together with the waits and barriers: the
 //    compiler cannot tell that an LDS read does not overlap the DMA writes still
@@ -27,9 +32,12 @@
 //    promotion acc += P * sa[m,kb] * sb[nb,kb] is one VALU FMA per output, the
 //    factor being one value per lane and sub-tile column because the MFMA
 //    operands are swapped (MFMA "A" = weight rows).  The partials are double
-//    buffered so the FMAs of one sub-tile run under the MFMAs of the next.
-//  * Tiles are numbered so that each XCD (workgroup id mod 8) works on one
-//    contiguous band of the tile grid, keeping its operand panels in its L2.
+//    buffered so the FMAs of one sub-tile run under the MFMAs of the next, and
+//    the FMAs of a block's last sub-tile run while the next block's fragments
+//    are read from LDS.
+//  * Dense tiles are numbered so that each XCD (workgroup id mod 8) works on one
+//    contiguous band of the tile grid, keeping its operand panels in its L2;
+//    grouped tiles put the m-tiles of one (expert, n-tile) next to each other.
 #include "launch.h"
 
 namespace fp8fg {
@@ -41,14 +49,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 256, BN = 256;
-constexpr int NTHREADS = 512;
-constexpr int TM = 64, TN = 128;  // wavefront tile (m, n)
-constexpr int SM = TM / 16, SN = TN / 16;
-constexpr int TILE_A = BM * 128;          // 32 KB
-constexpr int TILE_B = BN * 128;          // 32 KB
-constexpr int STAGE = TILE_A + TILE_B;    // 64 KB
-constexpr int GROUP_M = 4;                // m-tiles per band in the dense tile order
+constexpr int NTHREADS = 512;  // 8 wavefronts, 2 per SIMD
+constexpr int GROUP_M = 4;     // m-tiles per band in the dense tile order
 
 struct FParams {
   const uint8_t* a;
@@ -94,28 +96,47 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
 }
-// Wait until all of this wavefront's loads and LDS reads have completed, then
+// Wait until at most N of this wavefront's loads are outstanding (the newer
+// blocks and the L2 prefetch) and all of its LDS reads have completed, then
 // synchronise the workgroup: after it, the next K block is resident and the
 // stage read in this iteration may be refilled by any wavefront.
+template <int N>
 __device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-template <bool BF16OUT, bool GROUPED>
+// BM x BN output tile (m x n), WM x WN wavefronts, STAGES K blocks in LDS.
+template <int BM, int BN, int WM, int WN, int STAGES, bool BF16OUT, bool GROUPED>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) float s_sa[2][BM];
-  __shared__ __attribute__((aligned(16))) float s_sb[2][64];
+  static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
+  constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
+  constexpr int SM = TM / 16, SN = TN / 16;
+  static_assert(TN % 128 == 0 || 128 % TN == 0, "a wavefront's n range lies in one weight block");
+  constexpr int TILE_A = BM * 128;
+  constexpr int TILE_B = BN * 128;
+  constexpr int STAGE = TILE_A + TILE_B;
+  constexpr int A_DMA = BM / 64, B_DMA = BN / 64;  // 8-row DMAs per wavefront per stage
+  constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales
+  static_assert(SA_WAVES < 8, "one wavefront left for the weight-block scales");
+  // loads per wavefront per stage: tiles + one scale (or filler) DMA; the L2
+  // prefetch adds one more per iteration
+  constexpr int LOADS = A_DMA + B_DMA + 1;
+  constexpr int WAIT_N = (STAGES - 2) * LOADS + 1;
+  static_assert(STAGES >= 2, "at least double buffering");
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[STAGES * STAGE];
+  __shared__ __attribute__((aligned(16))) float s_sa[STAGES][BM];
+  __shared__ __attribute__((aligned(16))) float s_sb[STAGES][64];
+  __shared__ __attribute__((aligned(16))) float s_touch[8][64];  // L2-prefetch landing slots, never read
   __shared__ int tile_info[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2;  // 4 wavefronts along m, 2 along n
+  const int wm = wave % WM, wn = wave / WM;
 
   // ---- tile selection
   const int T = p.MT * p.NT;
@@ -192,47 +213,74 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   const int64_t n0 = static_cast<int64_t>(nt) * BN;
 
   // ---- per-lane source addresses (rows fixed for the whole K loop).
-  // Wavefront w fills rows [32w, 32w+32) of both tiles, 8 rows per DMA: lane L
-  // writes physical chunk L%8 of row 8i + L/8, i.e. logical chunk (L%8)^(L/8).
-  // Waves 0-3 also load the A scales of 64 rows each, wave 4 the two weight-block
-  // scales (lane 0: block n0/128, other lanes: block n0/128 + 1).
+  // Wavefront w fills A rows [w*BM/8, (w+1)*BM/8) and B rows [w*BN/8, ...),
+  // 8 rows per DMA: lane L writes physical chunk L%8 of row 8i + L/8, i.e.
+  // logical chunk (L%8)^(L/8).  Wavefronts 0..SA_WAVES-1 also load the A scales
+  // of 64 rows each, wavefront SA_WAVES the weight-block scales (lane i: block
+  // n0/128 + min(i, BN/128-1)); the others load a filler value into a scratch
+  // slot, so every wavefront issues exactly LOADS loads per stage.
   const int lrow = lane >> 3;
   const int lchunk = ((lane & 7) ^ lrow) * 16;
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
+  const uint8_t* ga[A_DMA];
+  const uint8_t* gb[B_DMA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + lrow;
+  for (int i = 0; i < A_DMA; ++i) {
+    const int r = wave * (BM / 8) + i * 8 + lrow;
     int64_t row = row_lo + r;
     row = row < row_hi ? row : row_hi - 1;
     ga[i] = p.a + row * p.K + lchunk;
-    gb[i] = bmat + (n0 + r) * p.K + lchunk;
   }
-  const float* gs = nullptr;
-  if (wave < 4) {
+#pragma unroll
+  for (int i = 0; i < B_DMA; ++i) gb[i] = bmat + (n0 + wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk;
+  // L2 prefetch of a future block: one 4-byte touch per 128-byte line, rows
+  // spread over the wavefronts (wavefront w covers tile rows 64w .. 64w+63 of
+  // the concatenated A|B row list, clamped to the last row).
+  const uint8_t* gt;
+  {
+    int r = wave * 64 + lane;
+    r = r < BM + BN ? r : BM + BN - 1;
+    if (r < BM) {
+      int64_t row = row_lo + r;
+      row = row < row_hi ? row : row_hi - 1;
+      gt = p.a + row * p.K;
+    } else {
+      gt = bmat + (n0 + r - BM) * p.K;
+    }
+  }
+  const float* gs;
+  if (wave < SA_WAVES) {
     int64_t row = row_lo + wave * 64 + lane;
     row = row < row_hi ? row : row_hi - 1;
     gs = p.sa + row * p.KB;
-  } else if (wave == 4) {
-    gs = bscale + (n0 / 128 + (lane < 1 ? 0 : 1)) * p.KB;
+  } else {
+    const int blk = lane < BN / 128 - 1 ? lane : BN / 128 - 1;
+    gs = bscale + (n0 / 128 + blk) * p.KB;
   }
   // wave-uniform LDS destinations (readfirstlane tells the compiler they are scalar)
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lds_ta = lds_addr(tiles) + uwave * 32 * 128;
-  const uint32_t lds_tb = lds_ta + TILE_A;
-  const uint32_t lds_s0 = uwave < 4 ? lds_addr(&s_sa[0][uwave * 64]) : lds_addr(&s_sb[0][0]);
-  const uint32_t lds_s_step = uwave < 4 ? BM * 4 : 64 * 4;
+  const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / 8) * 128;
+  const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (BN / 8) * 128;
+  const uint32_t lds_touch = lds_addr(&s_touch[uwave][0]);
+  const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
+                                           : (uwave == SA_WAVES ? lds_addr(&s_sb[0][0]) : lds_touch);
+  const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (uwave == SA_WAVES ? 64 * 4 : 0);
 
-  auto issue = [&](int kb, int st) {
+  constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
+  auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma16(ga[i] + kof, lds_ta + so + i * 1024);
-      dma16(gb[i] + kof, lds_tb + so + i * 1024);
-    }
-    if (uwave <= 4) dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step);
+    if (d < A_DMA)
+      dma16(ga[d] + kof, lds_ta + so + d * 1024);
+    else
+      dma16(gb[d - A_DMA] + kof, lds_tb + so + (d - A_DMA) * 1024);
   };
+  auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
+  auto issue = [&](int kb, int st) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma_tile(d, kb, st);
+    dma_scale(kb, st);
+  };
+  auto touch = [&](int kb) { dma4(gt + static_cast<int64_t>(kb) * 128, lds_touch); };
 
   v4f acc[SN][SM];
 #pragma unroll
@@ -241,33 +289,53 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     for (int j = 0; j < SM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int KB = p.KB;
-  issue(0, 0);
-  wait_barrier();
+  auto clampkb = [&](int kb) { return kb < KB ? kb : KB - 1; };
+  // prologue: blocks 0 .. STAGES-2 into stages 0 .. STAGES-2
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(clampkb(s0), s0);
+  touch(clampkb(STAGES - 1));
+  wait_barrier<WAIT_N>();  // block 0 resident
 
-  int st = 0;  // stage holding block kb
-  for (int kb = 0; kb < KB; ++kb) {
-    // Block kb+1 into the other stage (consumed in the previous iteration).  On
-    // the last iteration the free stage is refilled with block KB-1, which is
-    // not read again: the loop body stays branch-free.
-    issue(kb + 1 < KB ? kb + 1 : KB - 1, st ^ 1);
-
+  // Fragments of the current block: all m sub-tiles, the first n sub-tile, and
+  // the per-column promotion factors sa[m,kb] * sb[nb,kb].
+  v8i fm[SM];
+  float f[SM];
+  v8i fn;
+  auto load_frags = [&](int st) {
     const uint8_t* tA = tiles + st * STAGE;
     const uint8_t* tB = tA + TILE_A;
-    const float sbv = s_sb[st][wn];
-    v8i fm[SM];
-    float f[SM];
+    const float sbv = s_sb[st][(wn * TN) / 128];
 #pragma unroll
     for (int j = 0; j < SM; ++j) {
       fm[j] = frag(tA, wm * TM + j * 16, lane);
       f[j] = s_sa[st][wm * TM + j * 16 + (lane & 15)] * sbv;
     }
+    fn = frag(tB, wn * TN, lane);
+  };
+  load_frags(0);
+
+  int st = 0;  // stage holding block kb
+  v4f P[2][SM];
+  for (int kb = 0; kb < KB; ++kb) {
+    // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
+    // Near the end the free stage is refilled with block KB-1, which is not read
+    // again: the loop body stays branch-free and every wait is the same.
+    const int st_fill = st == 0 ? STAGES - 1 : st - 1;
+    const int kb_fill = clampkb(kb + STAGES - 1);
+    const uint8_t* tB = tiles + st * STAGE + TILE_A;
     // Software pipeline over the n sub-tiles: the fragment of sub-tile i+1 is
     // read from LDS while the MFMAs of sub-tile i run, and the promotion FMAs of
     // sub-tile i-1 (double-buffered partials) fill the VALU under them.
-    v4f P[2][SM];
-    v8i fn = frag(tB, wn * TN, lane);
 #pragma unroll
     for (int i = 0; i < SN; ++i) {
+      // The loads of the block being prefetched are spread over the sub-tile
+      // steps (about one DMA per step) instead of being issued together: the
+      // address unit then drains while the matrix cores run, and no wavefront
+      // stalls on a full memory-instruction queue before its MFMAs.
+#pragma unroll
+      for (int d = i * ND / SN; d < (i + 1) * ND / SN; ++d) dma_tile(d, kb_fill, st_fill);
+      if (i == 0) dma_scale(kb_fill, st_fill);
+      if (i == SN - 1) touch(clampkb(kb + STAGES));
       v8i fn_next;
       if (i + 1 < SN) fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
 #pragma unroll
@@ -282,23 +350,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
           for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = fmaf(P[(i - 1) & 1][j][r], f[j], acc[i - 1][j][r]);
       }
       if (i + 1 < SN) fn = fn_next;
-      // Issue order for this step: the next fragment's two LDS reads, then
-      // four times (one MFMA, four VALU FMAs of the previous sub-tile).
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-      for (int j = 0; j < SM; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
     }
+    float f_last[SM];
+#pragma unroll
+    for (int j = 0; j < SM; ++j) f_last[j] = f[j];
+
+    wait_barrier<WAIT_N>();  // block kb+1 resident; stage st free for refilling
+    st = st == STAGES - 1 ? 0 : st + 1;
+    // The next block's fragments are requested now, and the promotion of the
+    // last sub-tile of this block runs while they are in flight.  (After the
+    // final block this reads a stage nobody uses; the values are dropped.)
+    load_frags(st);
 #pragma unroll
     for (int j = 0; j < SM; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f[j], acc[SN - 1][j][r]);
-
-    wait_barrier();  // block kb+1 resident; stage st free for refilling
-    st ^= 1;
+      for (int r = 0; r < 4; ++r) acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_last[j], acc[SN - 1][j][r]);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
   // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
 #pragma unroll
@@ -320,28 +388,42 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   }
 }
 
-template <bool BF16OUT, bool GROUPED>
-hipError_t launch_fp8(const GemmArgs& g, int MT, hipStream_t s) {
+// Tile configurations: {BM, BN, WM, WN, STAGES}.
+//   0: 256 x 256, 4 x 2 wavefronts (64 x 128 each), 2 stages (128 KB LDS)
+//   1: 128 x 256, 2 x 4 wavefronts (64 x 64 each), 3 stages (144 KB LDS)
+template <int CFG> struct Cfg;
+template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
+template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
+
+template <int CFG, bool BF16OUT, bool GROUPED>
+hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
+  using C = Cfg<CFG>;
+  const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
   FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.M, g.N, g.K, g.G,
-            static_cast<int>(g.K / 128), MT, static_cast<int>(g.N / BN)};
-  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(MT) * p.NT);
-  hipLaunchKernelGGL((gemm_fp8_block_kernel<BF16OUT, GROUPED>), dim3(blocks), dim3(NTHREADS), 0, s, p);
+            static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN)};
+  const unsigned blocks = static_cast<unsigned>(MT * p.NT);
+  hipLaunchKernelGGL((gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, BF16OUT, GROUPED>), dim3(blocks),
+                     dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
+}
+
+template <int CFG>
+hipError_t launch_any(const GemmArgs& g, bool grouped, hipStream_t s) {
+  if (grouped) return g.y_bf16 ? launch_cfg<CFG, true, true>(g, s) : launch_cfg<CFG, false, true>(g, s);
+  return g.y_bf16 ? launch_cfg<CFG, true, false>(g, s) : launch_cfg<CFG, false, false>(g, s);
 }
 
 }  // namespace
 
 bool fp8_block_kernel_applies(const GemmArgs& g) {
-  return !g.exact && !g.row_scales && g.N % BN == 0;
+  return !g.exact && !g.row_scales && g.N % 256 == 0;
 }
 
+// Dense GEMMs use the 256 x 256 tile (least L2 traffic per flop).  Grouped
+// GEMMs use 128-row tiles: expert segments of ~256 rows then waste less of the
+// last m-tile of each segment, and the third stage hides the weight streaming.
 hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s) {
-  const int64_t MT = grouped ? g.M / BM + g.G : (g.M + BM - 1) / BM;
-  if (grouped)
-    return g.y_bf16 ? launch_fp8<true, true>(g, static_cast<int>(MT), s)
-                    : launch_fp8<false, true>(g, static_cast<int>(MT), s);
-  return g.y_bf16 ? launch_fp8<true, false>(g, static_cast<int>(MT), s)
-                  : launch_fp8<false, false>(g, static_cast<int>(MT), s);
+  return grouped ? launch_any<1>(g, true, s) : launch_any<0>(g, false, s);
 }
 
 }  // namespace fp8fg
