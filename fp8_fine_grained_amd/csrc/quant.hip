@@ -119,61 +119,98 @@ __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restr
 }
 
 // ------------------------------------------------------- 1x128, transposed
-// Input physically [K, ld] (e.g. tokens x channels); logical row m is column m.
-// Each lane owns COLS adjacent logical rows (bf16: 2, one dword of each
-// physical row; fp32: 1) over one 128-long group and keeps the 128 raw dwords
-// in registers, so a wavefront reads 64 contiguous dwords of each physical row.
+// Input physically [K, ld] (e.g. tokens x channels); logical row m is column m,
+// and a group is 128 consecutive physical rows (tokens) of one column.
+// A 512-thread block handles one 128-row x 256-byte tile (128 bf16 or 64 fp32
+// columns):
+//  1. the tile is read with full 256-byte row segments (16 lanes per row) and
+//     stored in LDS, the 16-byte chunks of row r XOR-permuted by
+//     ((r >> 4) & 7) << 1;
+//  2. thread (tg, d) reads dword d (2 bf16 / 1 fp32 columns) of rows
+//     16*tg .. 16*tg+15 -- with the permutation, the 64 lanes of a wavefront hit
+//     64 distinct banks -- reduces the amax over the 8 token groups of its
+//     columns with lane shuffles, and writes its 16 codes per column as one
+//     16-byte store (8 threads write a column's 128 codes contiguously).
+constexpr int kColsTileBytes = 256;
+__device__ __forceinline__ int cols_swz(int row) { return ((row >> 4) & 7) << 1; }
+
 template <bool BF16>
-__global__ void __launch_bounds__(256) quant_act_cols_kernel(const void* __restrict__ x, int64_t ld,
-                                                             int64_t M, int G,
+__global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restrict__ x, int64_t ld,
+                                                             int64_t M, int G, int CB,
                                                              uint8_t* __restrict__ q,
                                                              float* __restrict__ scales, int64_t K) {
-  constexpr int COLS = BF16 ? 2 : 1;
-  const int64_t lane_col = static_cast<int64_t>(blockIdx.x) * 64 + (threadIdx.x & 63);
-  const int g = static_cast<int>(blockIdx.y) * 4 + (threadIdx.x >> 6);
-  const int64_t m0 = lane_col * COLS;
-  if (m0 >= M || g >= G) return;  // no cross-lane operations below
-  const int64_t k0 = static_cast<int64_t>(g) * 128;
-  const int64_t step = ld / COLS;  // dwords per physical row
-  const uint32_t* base = static_cast<const uint32_t*>(x) + (k0 * ld + m0) / COLS;
-  uint32_t w[128];
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int COLS_PER_DW = BF16 ? 2 : 1;
+  constexpr int TILE_COLS = kColsTileBytes / ES;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * kColsTileBytes];
+  const int tid = threadIdx.x;
+  const int cb = blockIdx.x % CB;  // column block
+  const int g = blockIdx.x / CB;   // token group
+  const int64_t col0 = static_cast<int64_t>(cb) * TILE_COLS;
+  const int64_t row0 = static_cast<int64_t>(g) * 128;
+
+  // 1. global -> LDS: thread t moves chunks (row t/16 + 32i, chunk t%16), i = 0..3.
+  {
+    const int c = tid & 15;
+    int64_t ccol = col0 + c * (16 / ES);  // first column of the chunk
+    const bool cvalid = ccol < M;         // M % 8 == 0: a chunk is all in or all out
+    if (!cvalid) ccol = col0;             // stay inside the row; the data is never stored
 #pragma unroll
-  for (int t = 0; t < 128; ++t) w[t] = __builtin_nontemporal_load(base + t * step);
+    for (int i = 0; i < 4; ++i) {
+      const int r = (tid >> 4) + 32 * i;
+      const u32x4 v = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const char*>(x) + ((row0 + r) * ld + ccol) * ES));
+      *reinterpret_cast<u32x4*>(tile + r * kColsTileBytes + ((c ^ cols_swz(r)) * 16)) = v;
+    }
+  }
+  __syncthreads();
+
+  // 2. thread (tg, d): lane = 8*d_local... wavefront w owns dwords 8w .. 8w+7.
+  const int lane = tid & 63;
+  const int tg = lane >> 3;                      // token group: rows 16*tg .. +15
+  const int d = (tid >> 6) * 8 + (lane & 7);     // dword of the 256-byte row, 0..63
+  const int chunk = d >> 2, within = (d & 3) * 4;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * tg + i;
+    w[i] = *reinterpret_cast<const uint32_t*>(tile + r * kColsTileBytes + ((chunk ^ cols_swz(r)) * 16) + within);
+  }
   auto lo = [](uint32_t u) { return BF16 ? bf16_lo(u) : __uint_as_float(u); };
   float amax0 = 0.0f, amax1 = 0.0f;
 #pragma unroll
-  for (int t = 0; t < 128; ++t) {
-    amax0 = fmaxf(amax0, fabsf(lo(w[t])));
-    if constexpr (BF16) amax1 = fmaxf(amax1, fabsf(bf16_hi(w[t])));
+  for (int i = 0; i < 16; ++i) {
+    amax0 = fmaxf(amax0, fabsf(lo(w[i])));
+    if constexpr (BF16) amax1 = fmaxf(amax1, fabsf(bf16_hi(w[i])));
   }
-  float s0, inv0, s1 = 0.0f, inv1 = 0.0f;
+  // reduce over the 8 token groups (lanes l, l+8, ..., l+56)
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) {
+    amax0 = fmaxf(amax0, __shfl_xor(amax0, o));
+    if constexpr (BF16) amax1 = fmaxf(amax1, __shfl_xor(amax1, o));
+  }
+  const int64_t m0 = col0 + static_cast<int64_t>(d) * COLS_PER_DW;
+  if (m0 >= M) return;  // no cross-lane operations below
+  float s0, inv0;
   group_scale(amax0, s0, inv0);
-  if constexpr (BF16) group_scale(amax1, s1, inv1);
-  u32x4* qa = reinterpret_cast<u32x4*>(q + m0 * K + k0);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int t = c * 16;
-    u32x4 o;
-    o.x = cvt4(lo(w[t]) * inv0, lo(w[t + 1]) * inv0, lo(w[t + 2]) * inv0, lo(w[t + 3]) * inv0);
-    o.y = cvt4(lo(w[t + 4]) * inv0, lo(w[t + 5]) * inv0, lo(w[t + 6]) * inv0, lo(w[t + 7]) * inv0);
-    o.z = cvt4(lo(w[t + 8]) * inv0, lo(w[t + 9]) * inv0, lo(w[t + 10]) * inv0, lo(w[t + 11]) * inv0);
-    o.w = cvt4(lo(w[t + 12]) * inv0, lo(w[t + 13]) * inv0, lo(w[t + 14]) * inv0, lo(w[t + 15]) * inv0);
-    __builtin_nontemporal_store(o, qa + c);
-  }
-  scales[m0 * G + g] = s0;
+  const int64_t k0 = row0 + 16 * tg;
+  u32x4 o;
+  o.x = cvt4(lo(w[0]) * inv0, lo(w[1]) * inv0, lo(w[2]) * inv0, lo(w[3]) * inv0);
+  o.y = cvt4(lo(w[4]) * inv0, lo(w[5]) * inv0, lo(w[6]) * inv0, lo(w[7]) * inv0);
+  o.z = cvt4(lo(w[8]) * inv0, lo(w[9]) * inv0, lo(w[10]) * inv0, lo(w[11]) * inv0);
+  o.w = cvt4(lo(w[12]) * inv0, lo(w[13]) * inv0, lo(w[14]) * inv0, lo(w[15]) * inv0);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + m0 * K + k0));
+  if (tg == 0) scales[m0 * G + g] = s0;
   if constexpr (BF16) {
-    u32x4* qb = reinterpret_cast<u32x4*>(q + (m0 + 1) * K + k0);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int t = c * 16;
-      u32x4 o;
-      o.x = cvt4(bf16_hi(w[t]) * inv1, bf16_hi(w[t + 1]) * inv1, bf16_hi(w[t + 2]) * inv1, bf16_hi(w[t + 3]) * inv1);
-      o.y = cvt4(bf16_hi(w[t + 4]) * inv1, bf16_hi(w[t + 5]) * inv1, bf16_hi(w[t + 6]) * inv1, bf16_hi(w[t + 7]) * inv1);
-      o.z = cvt4(bf16_hi(w[t + 8]) * inv1, bf16_hi(w[t + 9]) * inv1, bf16_hi(w[t + 10]) * inv1, bf16_hi(w[t + 11]) * inv1);
-      o.w = cvt4(bf16_hi(w[t + 12]) * inv1, bf16_hi(w[t + 13]) * inv1, bf16_hi(w[t + 14]) * inv1, bf16_hi(w[t + 15]) * inv1);
-      __builtin_nontemporal_store(o, qb + c);
-    }
-    scales[(m0 + 1) * G + g] = s1;
+    float s1, inv1;
+    group_scale(amax1, s1, inv1);
+    u32x4 h;
+    h.x = cvt4(bf16_hi(w[0]) * inv1, bf16_hi(w[1]) * inv1, bf16_hi(w[2]) * inv1, bf16_hi(w[3]) * inv1);
+    h.y = cvt4(bf16_hi(w[4]) * inv1, bf16_hi(w[5]) * inv1, bf16_hi(w[6]) * inv1, bf16_hi(w[7]) * inv1);
+    h.z = cvt4(bf16_hi(w[8]) * inv1, bf16_hi(w[9]) * inv1, bf16_hi(w[10]) * inv1, bf16_hi(w[11]) * inv1);
+    h.w = cvt4(bf16_hi(w[12]) * inv1, bf16_hi(w[13]) * inv1, bf16_hi(w[14]) * inv1, bf16_hi(w[15]) * inv1);
+    __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(q + (m0 + 1) * K + k0));
+    if (tg == 0) scales[(m0 + 1) * G + g] = s1;
   }
 }
 
@@ -249,12 +286,13 @@ hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K,
 hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s) {
   const int G = static_cast<int>(K / 128);
-  const int64_t lane_cols = bf16 ? (M + 1) / 2 : M;
-  const dim3 grid(static_cast<unsigned>((lane_cols + 63) / 64), static_cast<unsigned>((G + 3) / 4));
+  const int tile_cols = kColsTileBytes / (bf16 ? 2 : 4);
+  const int CB = static_cast<int>((M + tile_cols - 1) / tile_cols);
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(CB) * G));
   if (bf16)
-    hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(256), 0, s, x, ld, M, G, q, scales, K);
+    hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(512), 0, s, x, ld, M, G, CB, q, scales, K);
   else
-    hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(256), 0, s, x, ld, M, G, q, scales, K);
+    hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(512), 0, s, x, ld, M, G, CB, q, scales, K);
   return hipGetLastError();
 }
 
