@@ -37,22 +37,18 @@ def _sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _traffic(record_name, kernel_src, launches_bytes_key="per_launch_bytes"):
+def _traffic(record_name, kernel_src):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None.
 
     The summary records the sha256 of the kernel source it was taken with; if
     the source has changed since, the figure no longer applies and None is
     returned."""
-    path = os.path.join(ROOT, "profiles", record_name)
-    if not os.path.exists(path):
+    from fp8_fine_grained_amd.profile_summary import load_traffic
+
+    rec = load_traffic(os.path.join(ROOT, "profiles", record_name))
+    if not rec or rec.get("kernel_source_sha256") != _sha(kernel_src):
         return None
-    try:
-        rec = json.load(open(path))
-    except Exception:
-        return None
-    if rec.get("kernel_source_sha256") != _sha(kernel_src):
-        return None
-    return rec.get(launches_bytes_key)
+    return rec.get("per_launch_bytes")
 
 
 class Timer:
@@ -133,8 +129,8 @@ def bench_dense(args, torch, fp8, workloads):
     act_bytes = M * K * (2 + 1) + M * (K // 128) * 4
     w_bytes = N * K * (2 + 1) + (N // 128) * (K // 128) * 4
     gemm_tflops = flop / (gemm_ms * 1e-3) / 1e12
-    traffic = _traffic("block_gemm_dense_4096x7168x7168_traffic.json",
-                       os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm.hip"))
+    traffic = _traffic("block_gemm_dense_4096x7168x7168_traffic.md",
+                       os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip"))
     out = {
         "metric": "FP8 block-scaled GEMM TFLOP/s (% dense FP8 peak); quantizer GB/s (% HBM peak)",
         "value": flop / dt / 1e12,
@@ -177,12 +173,11 @@ def bench_dense(args, torch, fp8, workloads):
 
 
 def cpu_baseline_dense(d):
-    """The oracle on a bounded sample of the dense step: 256 rows of X, all of W."""
-    import numpy as np
-
+    """The oracle on the dense step itself (all 4096 rows of X, all of W): a few
+    seconds to tens of seconds of host time, depending on the host's cores."""
     from oracle import gemm, quant
 
-    rows = 256
+    rows = d["x"].shape[0]
     x = d["x"][:rows].float().numpy()
     w = d["w"].float().numpy()
     t0 = time.perf_counter()
@@ -191,10 +186,9 @@ def cpu_baseline_dense(d):
     gemm.block_gemm(ra, rsa, rb, rsb)
     dt = time.perf_counter() - t0
     flop = 2.0 * rows * w.shape[0] * w.shape[1]
-    del np
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"dense step on X rows 0..{rows - 1} of [4096,7168] with the full W [7168,7168]: "
-                      f"numpy 1x128 + 128x128 quantisation and fp64 GEMM; {dt:.1f} s"}
+            "sample": f"one dense step, X [{rows},7168] and W [7168,7168]: numpy 1x128 + 128x128 "
+                      f"quantisation (one thread) and fp64 GEMM (BLAS threads); {dt:.1f} s"}
 
 
 # ------------------------------------------------------------------ other rows
@@ -242,7 +236,7 @@ def bench_quant(args, torch, fp8, workloads):
         "kernels": {"fp8_quant_act_1x128": act_line, "fp8_quant_weight_128x128": w_line},
         "roofline": {"bound": "hbm", "achieved": act_line["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": act_line["frac_hbm"],
-                     "traffic": _traffic("quant_act_1x128_16384x7168_traffic.json",
+                     "traffic": _traffic("quant_act_1x128_16384x7168_traffic.md",
                                          os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "quant.hip"))},
     }
 
@@ -296,8 +290,8 @@ def bench_moe(args, torch, fp8, workloads):
         },
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                     "traffic": _traffic("grouped_gemm_moe_65536x2048x7168_traffic.json",
-                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm.hip"))},
+                     "traffic": _traffic("grouped_gemm_moe_65536x2048x7168_traffic.md",
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip"))},
     }
 
 

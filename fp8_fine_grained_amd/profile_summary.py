@@ -1,0 +1,144 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+Usage (from the repository root, after copying rocprofv3 output back):
+
+    python -m fp8_fine_grained_amd.profile_summary stats <kernel_stats.csv> <out.md> "<command>"
+    python -m fp8_fine_grained_amd.profile_summary traffic <fetch.csv> <write.csv> \
+        <calib_fetch.csv> <calib_write.csv> <kernel-substring> <kernel-source> <out.md> \
+        "<fetch command>" "<write command>" "<calibration commands>"
+
+``traffic`` averages the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch)
+over the dispatches whose name contains the substring, and scales each by what
+the same counter reads for a plain device-to-device copy of 1 GiB (the largest
+dispatch of the calibration run): bytes = counter * 1024 * (known / measured).
+The summary records the sha256 of the kernel source it was measured with;
+``bench.py`` only reports the traffic while that source is unchanged.
+"""
+
+import csv
+import hashlib
+import json
+import sys
+
+COPY_BYTES = 1 << 30
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def stats(csv_path, out_md, command):
+    rows = _rows(csv_path)
+    lines = [
+        "# rocprofv3 kernel statistics",
+        "",
+        "Command (repository root on the GPU box):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        "| kernel | calls | average (us) | min (us) | max (us) | share |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 110:
+            name = name[:107] + "..."
+        lines.append(
+            f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+            f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _mean_counter(path, counter, substr=None, largest=False):
+    vals = []
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        if substr is not None and substr not in r["Kernel_Name"]:
+            continue
+        vals.append((float(r["Counter_Value"]), r["Kernel_Name"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows matching {substr!r} in {path}")
+    if largest:
+        v = max(vals)
+        return v[0], v[1], 1
+    return sum(v for v, _ in vals) / len(vals), vals[0][1], len(vals)
+
+
+def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, substr, kernel_src, out_md,
+            fetch_cmd, write_cmd, cal_cmd):
+    f_kib, name, nf = _mean_counter(fetch_csv, "FETCH_SIZE", substr)
+    w_kib, _, nw = _mean_counter(write_csv, "WRITE_SIZE", substr)
+    cf_kib, cname, _ = _mean_counter(cal_fetch_csv, "FETCH_SIZE", largest=True)
+    cw_kib, _, _ = _mean_counter(cal_write_csv, "WRITE_SIZE", largest=True)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    fetch_bytes = f_kib * 1024.0 * f_scale
+    write_bytes = w_kib * 1024.0 * w_scale
+    with open(kernel_src, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    rec = {
+        "kernel": name[:200],
+        "kernel_source": kernel_src,
+        "kernel_source_sha256": sha,
+        "dispatches_averaged": {"fetch": nf, "write": nw},
+        "fetch_kib_raw": f_kib,
+        "write_kib_raw": w_kib,
+        "copy_calibration": {"bytes": COPY_BYTES, "kernel": cname[:120], "fetch_kib": cf_kib,
+                             "write_kib": cw_kib, "fetch_scale": f_scale, "write_scale": w_scale},
+        "fetch_bytes": fetch_bytes,
+        "write_bytes": write_bytes,
+        "per_launch_bytes": fetch_bytes + write_bytes,
+    }
+    lines = [
+        "# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)",
+        "",
+        f"Kernel: `{name[:160]}`",
+        "",
+        "Commands (repository root on the GPU box, one counter per run):",
+        "",
+        "```",
+        fetch_cmd,
+        write_cmd,
+        cal_cmd,
+        "```",
+        "",
+        f"- FETCH_SIZE {f_kib:.0f} KiB/dispatch x {f_scale:.4f} = {fetch_bytes / 1e6:.1f} MB",
+        f"- WRITE_SIZE {w_kib:.0f} KiB/dispatch x {w_scale:.4f} = {write_bytes / 1e6:.1f} MB",
+        f"- calibration: 1 GiB copy read {cf_kib:.0f} KiB, wrote {cw_kib:.0f} KiB",
+        "",
+        "```json",
+        json.dumps(rec, indent=1),
+        "```",
+    ]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def load_traffic(md_path):
+    """The JSON record embedded in a traffic summary (None if absent)."""
+    try:
+        text = open(md_path).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    try:
+        return json.loads(text[start + 7:end])
+    except ValueError:
+        return None
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(*sys.argv[2:5])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:12])
+    else:
+        raise SystemExit(__doc__)
