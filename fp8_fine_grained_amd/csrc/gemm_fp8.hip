@@ -14,10 +14,10 @@
 //    (128-row tiles waste less of the last tile of each ~256-row expert segment).
 //    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
 //  * One 128-wide K block per LDS stage; the loads of block kb+STAGES-1 are in
-//    flight while block kb is multiplied, spread over the sub-tile steps (about
-//    one DMA per step) so the address unit drains while the matrix cores run.
-//    One further block is only touched: one 4-byte DMA per 128-byte line (into a
-//    scratch LDS slot nobody reads) pulls it into L2 ahead of its real loads.
+//    flight while block kb is multiplied.  They are issued over the first half
+//    of the sub-tile steps (a few DMAs per step, between MFMAs): early enough to
+//    land before the end of the iteration, spread enough that no wavefront
+//    stalls on a full memory-instruction queue before its first MFMAs.
 //  * Tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    issued through inline assembly together with the waits and barriers: the
 //    compiler cannot tell that an LDS read does not overlap the DMA writes still
@@ -32,9 +32,10 @@
 //    promotion acc += P * sa[m,kb] * sb[nb,kb] is one VALU FMA per output, the
 //    factor being one value per lane and sub-tile column because the MFMA
 //    operands are swapped (MFMA "A" = weight rows).  The partials are double
-//    buffered so the FMAs of one sub-tile run under the MFMAs of the next, and
-//    the FMAs of a block's last sub-tile run while the next block's fragments
-//    are read from LDS.
+//    buffered so the FMAs of one sub-tile run under the MFMAs of the next.  The
+//    barrier of each K block comes right after its last LDS read: the last
+//    sub-tile's MFMAs and FMAs run after it, while the next block's fragments
+//    are being read.
 //  * Dense tiles are numbered so that each XCD (workgroup id mod 8) works on one
 //    contiguous band of the tile grid, keeping its operand panels in its L2;
 //    grouped tiles put the m-tiles of one (expert, n-tile) next to each other.
@@ -96,8 +97,8 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
 }
-// Wait until at most N of this wavefront's loads are outstanding (the newer
-// blocks and the L2 prefetch) and all of its LDS reads have completed, then
+// Wait until at most N of this wavefront's loads are outstanding (those of the
+// newer blocks) and all of its LDS reads have completed, then
 // synchronise the workgroup: after it, the next K block is resident and the
 // stage read in this iteration may be refilled by any wavefront.
 template <int N>
@@ -122,15 +123,19 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   constexpr int A_DMA = BM / 64, B_DMA = BN / 64;  // 8-row DMAs per wavefront per stage
   constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales
   static_assert(SA_WAVES < 8, "one wavefront left for the weight-block scales");
-  // loads per wavefront per stage: tiles + one scale (or filler) DMA; the L2
-  // prefetch adds one more per iteration
+  // loads per wavefront per stage: tiles + one scale (or filler) DMA
   constexpr int LOADS = A_DMA + B_DMA + 1;
-  constexpr int WAIT_N = (STAGES - 2) * LOADS + 1;
+  constexpr int WAIT_N = (STAGES - 2) * LOADS;
   static_assert(STAGES >= 2, "at least double buffering");
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[STAGES * STAGE];
+  // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
+  // padded by 16) in its own slice of the tile buffer.
+  constexpr int EPI_PITCH = TN * 2 + 16;
+  constexpr int EPI_BYTES = 8 * TM * EPI_PITCH;
+  constexpr int TILES_BYTES = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[TILES_BYTES];
   __shared__ __attribute__((aligned(16))) float s_sa[STAGES][BM];
   __shared__ __attribute__((aligned(16))) float s_sb[STAGES][64];
-  __shared__ __attribute__((aligned(16))) float s_touch[8][64];  // L2-prefetch landing slots, never read
+  __shared__ __attribute__((aligned(16))) float s_filler[64];  // landing slot of the filler DMAs, never read
   __shared__ int tile_info[3];
 
   const int tid = threadIdx.x;
@@ -232,21 +237,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   }
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) gb[i] = bmat + (n0 + wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk;
-  // L2 prefetch of a future block: one 4-byte touch per 128-byte line, rows
-  // spread over the wavefronts (wavefront w covers tile rows 64w .. 64w+63 of
-  // the concatenated A|B row list, clamped to the last row).
-  const uint8_t* gt;
-  {
-    int r = wave * 64 + lane;
-    r = r < BM + BN ? r : BM + BN - 1;
-    if (r < BM) {
-      int64_t row = row_lo + r;
-      row = row < row_hi ? row : row_hi - 1;
-      gt = p.a + row * p.K;
-    } else {
-      gt = bmat + (n0 + r - BM) * p.K;
-    }
-  }
   const float* gs;
   if (wave < SA_WAVES) {
     int64_t row = row_lo + wave * 64 + lane;
@@ -260,12 +250,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / 8) * 128;
   const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (BN / 8) * 128;
-  const uint32_t lds_touch = lds_addr(&s_touch[uwave][0]);
   const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
-                                           : (uwave == SA_WAVES ? lds_addr(&s_sb[0][0]) : lds_touch);
+                                           : (uwave == SA_WAVES ? lds_addr(&s_sb[0][0]) : lds_addr(s_filler));
   const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (uwave == SA_WAVES ? 64 * 4 : 0);
 
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
+  constexpr int SPREAD = SN >= 4 ? SN / 2 : SN;  // sub-tile steps that issue them
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
@@ -280,7 +270,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     for (int d = 0; d < ND; ++d) dma_tile(d, kb, st);
     dma_scale(kb, st);
   };
-  auto touch = [&](int kb) { dma4(gt + static_cast<int64_t>(kb) * 128, lds_touch); };
 
   v4f acc[SN][SM];
 #pragma unroll
@@ -293,11 +282,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // prologue: blocks 0 .. STAGES-2 into stages 0 .. STAGES-2
 #pragma unroll
   for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(clampkb(s0), s0);
-  touch(clampkb(STAGES - 1));
   wait_barrier<WAIT_N>();  // block 0 resident
 
   // Fragments of the current block: all m sub-tiles, the first n sub-tile, and
-  // the per-column promotion factors sa[m,kb] * sb[nb,kb].
+  // the per-column promotion factors sa[m,kb] * sb[nb,kb] (block 0 here; the
+  // loop requests each next block's right after its barrier).
   v8i fm[SM];
   float f[SM];
   v8i fn;
@@ -323,21 +312,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     const int st_fill = st == 0 ? STAGES - 1 : st - 1;
     const int kb_fill = clampkb(kb + STAGES - 1);
     const uint8_t* tB = tiles + st * STAGE + TILE_A;
-    // Software pipeline over the n sub-tiles: the fragment of sub-tile i+1 is
-    // read from LDS while the MFMAs of sub-tile i run, and the promotion FMAs of
-    // sub-tile i-1 (double-buffered partials) fill the VALU under them.
+    __builtin_amdgcn_s_setprio(1);  // the issuing phase of the matrix cores goes first
+    // Sub-tile steps 0 .. SN-2: the fragment of step i+1 is read from LDS while
+    // the MFMAs of step i run, and the promotion FMAs of step i-1 (double-
+    // buffered partials) fill the VALU under them.
 #pragma unroll
-    for (int i = 0; i < SN; ++i) {
-      // The loads of the block being prefetched are spread over the sub-tile
-      // steps (about one DMA per step) instead of being issued together: the
-      // address unit then drains while the matrix cores run, and no wavefront
-      // stalls on a full memory-instruction queue before its MFMAs.
+    for (int i = 0; i < SN - 1; ++i) {
+      // The loads of the block being prefetched go out over the first SPREAD
+      // sub-tile steps, between MFMAs.
+      if (i < SPREAD) {
 #pragma unroll
-      for (int d = i * ND / SN; d < (i + 1) * ND / SN; ++d) dma_tile(d, kb_fill, st_fill);
+        for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
+      }
       if (i == 0) dma_scale(kb_fill, st_fill);
-      if (i == SN - 1) touch(clampkb(kb + STAGES));
-      v8i fn_next;
-      if (i + 1 < SN) fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
+      const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
 #pragma unroll
       for (int j = 0; j < SM; ++j) {
         const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -349,39 +337,80 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = fmaf(P[(i - 1) & 1][j][r], f[j], acc[i - 1][j][r]);
       }
-      if (i + 1 < SN) fn = fn_next;
+      fn = fn_next;
     }
-    float f_last[SM];
-#pragma unroll
-    for (int j = 0; j < SM; ++j) f_last[j] = f[j];
 
-    wait_barrier<WAIT_N>();  // block kb+1 resident; stage st free for refilling
+    // Every LDS read of this stage has been issued: once they have returned and
+    // block kb+1 is resident, the workgroup synchronises.  The last step's MFMAs
+    // run after the barrier, and the next block's fragments are requested as
+    // each m fragment is consumed, so their LDS latency hides under the MFMAs.
+    __builtin_amdgcn_s_setprio(0);
+    wait_barrier<WAIT_N>();
     st = st == STAGES - 1 ? 0 : st + 1;
-    // The next block's fragments are requested now, and the promotion of the
-    // last sub-tile of this block runs while they are in flight.  (After the
-    // final block this reads a stage nobody uses; the values are dropped.)
-    load_frags(st);
+    float f_old[SM];
+#pragma unroll
+    for (int j = 0; j < SM; ++j) f_old[j] = f[j];
+    {
+      const uint8_t* tA = tiles + st * STAGE;
+      const float sbv = s_sb[st][(wn * TN) / 128];
+#pragma unroll
+      for (int j = 0; j < SM; ++j) {
+        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+        P[(SN - 1) & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fn, fm[j], z, 0, 0, 0, 0, 0, 0);
+        // (After the final block this reads a stage nobody uses; the values are dropped.)
+        fm[j] = frag(tA, wm * TM + j * 16, lane);
+        f[j] = s_sa[st][wm * TM + j * 16 + (lane & 15)] * sbv;
+      }
+      fn = frag(tA + TILE_A, wn * TN, lane);
+    }
 #pragma unroll
     for (int j = 0; j < SM; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_last[j], acc[SN - 1][j][r]);
+      for (int r = 0; r < 4; ++r) acc[SN - 2][j][r] = fmaf(P[(SN - 2) & 1][j][r], f_old[j], acc[SN - 2][j][r]);
+#pragma unroll
+    for (int j = 0; j < SM; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_old[j], acc[SN - 1][j][r]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
   // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
+  __syncthreads();  // every wavefront is done with the tile buffers
+  if constexpr (BF16OUT) {
+    // Stage the wavefront's TM x TN block as bf16 rows in LDS (8 bytes per lane
+    // and sub-tile), then write whole row segments (TN*2 bytes = 16 lanes x 16 B).
+    uint8_t* epi = tiles + wave * TM * EPI_PITCH;
 #pragma unroll
-  for (int j = 0; j < SM; ++j) {
-    const int64_t m = row_lo + wm * TM + j * 16 + (lane & 15);
-    if (m >= row_hi) continue;
+    for (int j = 0; j < SM; ++j)
 #pragma unroll
-    for (int i = 0; i < SN; ++i) {
-      const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
-      if constexpr (BF16OUT) {
+      for (int i = 0; i < SN; ++i) {
+        const int mr = j * 16 + (lane & 15);
+        const int nc = i * 16 + 4 * (lane >> 4);
         u32x2 o;
         o[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
         o[1] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.y) + m * p.N + n) = o;
-      } else {
+        *reinterpret_cast<u32x2*>(epi + mr * EPI_PITCH + nc * 2) = o;
+      }
+    // (ds ops of one wavefront complete in order: no barrier needed here)
+    constexpr int LANES_PER_ROW = TN * 2 / 16;
+    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+    const int c16 = lane % LANES_PER_ROW;
+#pragma unroll
+    for (int pass = 0; pass < TM / ROWS_PER_PASS; ++pass) {
+      const int mr = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      const int64_t m = row_lo + wm * TM + mr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * EPI_PITCH + c16 * 16);
+      if (m < row_hi)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + m * p.N + n0 + wn * TN + c16 * 8) = v;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SM; ++j) {
+      const int64_t m = row_lo + wm * TM + j * 16 + (lane & 15);
+      if (m >= row_hi) continue;
+#pragma unroll
+      for (int i = 0; i < SN; ++i) {
+        const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
         *reinterpret_cast<v4f*>(static_cast<float*>(p.y) + m * p.N + n) = acc[i][j];
       }
     }
