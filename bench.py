@@ -52,29 +52,69 @@ def _traffic(record_name, kernel_src):
 
 
 class Timer:
-    """HIP-event timing of one kernel launch site on torch's current stream."""
+    """HIP-event timing of one kernel launch site on the stream it is launched on.
 
-    def __init__(self, torch):
+    The events are created with hipEventReleaseToDevice.  A default event
+    performs a system-scope release when it is recorded, which writes the
+    dirty L2 lines back to HBM (after the dense GEMM that is its whole bf16
+    output) and so adds that write-back to the bracketed launch; a
+    device-scope release times the launch alone."""
+
+    _lib = None
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self, torch, n=64):
+        """n: the most launches this timer will bracket (its events are created
+        here, outside the timed region)."""
+        import ctypes
+
         self.torch = torch
-        self.pairs = []
+        self.ct = ctypes
+        if Timer._lib is None:
+            torch.cuda.init()
+            lib = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch has already loaded
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            Timer._lib = lib
+        self.lib = Timer._lib
+        self.events = []
+        for _ in range(2 * n):
+            ev = ctypes.c_void_p()
+            rc = self.lib.hipEventCreateWithFlags(ctypes.byref(ev), self.RELEASE_TO_DEVICE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.events.append(ev)
+        self.used = 0
+
+    def _record(self):
+        if self.used >= len(self.events):
+            raise RuntimeError("Timer: more launches than events created")
+        ev = self.events[self.used]
+        self.used += 1
+        rc = self.lib.hipEventRecord(ev, self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def __enter__(self):
-        s = self.torch.cuda.Event(enable_timing=True)
-        s.record()
-        self.pairs.append([s, None])
+        self._record()
         return self
 
     def __exit__(self, *a):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs[-1][1] = e
+        self._record()
 
     def mean_ms(self):
-        ts = [s.elapsed_time(e) for s, e in self.pairs]
+        self.torch.cuda.synchronize()
+        ts = []
+        for i in range(0, self.used, 2):
+            ms = self.ct.c_float()
+            rc = self.lib.hipEventElapsedTime(self.ct.byref(ms), self.events[i], self.events[i + 1])
+            if rc != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+            ts.append(ms.value)
         return sum(ts) / len(ts) if ts else float("nan")
-
-    def reset(self):
-        self.pairs = []
 
 
 def _cpu_threads():
@@ -99,7 +139,7 @@ def bench_dense(args, torch, fp8, workloads):
     qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
     sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-    t_act, t_w, t_gemm = Timer(torch), Timer(torch), Timer(torch)
+    t_act, t_w, t_gemm = Timer(torch, args.steps), Timer(torch, args.steps), Timer(torch, args.steps)
 
     def step(i, timed):
         x, w = xs[i % 3], ws[i % 3]
@@ -209,7 +249,7 @@ def bench_quant(args, torch, fp8, workloads):
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     qw = torch.empty((N, KW), dtype=torch.uint8, device="cuda")
     sw = torch.empty((N // 128, KW // 128), dtype=torch.float32, device="cuda")
-    ta, tw = Timer(torch), Timer(torch)
+    ta, tw = Timer(torch, args.steps), Timer(torch, args.steps)
     for i in range(args.warmup):
         fp8.fp8_quant_act_1x128(acts[i % 3], qa, sa)
         fp8.fp8_quant_weight_128x128(ws[i % 3], qw, sw)
@@ -258,7 +298,7 @@ def bench_moe(args, torch, fp8, workloads):
     qa = torch.empty((Mt, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((Mt, K // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
-    tq, tg = Timer(torch), Timer(torch)
+    tq, tg = Timer(torch, args.steps), Timer(torch, args.steps)
     for _ in range(args.warmup):
         fp8.fp8_quant_act_1x128(xa, qa, sa)
         fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
@@ -304,7 +344,7 @@ def bench_wgrad(args, torch, fp8, workloads):
     qb = torch.empty((C, T), dtype=torch.uint8, device="cuda")
     sb = torch.empty((C, T // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((C, C), dtype=torch.float32, device="cuda")
-    tq, tg, tf = Timer(torch), Timer(torch), Timer(torch)
+    tq, tg, tf = Timer(torch, args.steps), Timer(torch, args.steps), Timer(torch, args.steps)
     for _ in range(args.warmup):
         fp8.fp8_quant_act_1x128(dy.t(), qa, sa)
         fp8.fp8_quant_act_1x128(x.t(), qb, sb)

@@ -87,12 +87,14 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row0, int lane) {
   return f;
 }
 
-// LDS DMA: 64 lanes x 16 bytes (or 4 bytes) from per-lane global addresses to
-// 1 KB (256 B) of LDS starting at the wave-uniform byte address `lds`.
+// LDS DMA: 64 lanes x 16 bytes (or 4 bytes) to 1 KB (256 B) of LDS starting
+// at the wave-uniform byte address `lds`.  The tile form takes a wave-uniform
+// base (SGPR pair) plus a fixed 32-bit per-lane offset, so advancing to the
+// next K block is a scalar add and the instruction reads one address VGPR.
 // M0 is written here and nowhere else in the kernel (no other instruction of
 // this kernel reads M0), so it needs no saving.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory");
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
@@ -104,6 +106,14 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
 template <int N>
 __device__ __forceinline__ void wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+// A pointer every lane holds the same value of, moved to scalar registers.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -136,7 +146,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   __shared__ __attribute__((aligned(16))) float s_sa[STAGES][BM];
   __shared__ __attribute__((aligned(16))) float s_sb[STAGES][64];
   __shared__ __attribute__((aligned(16))) float s_filler[64];  // landing slot of the filler DMAs, never read
-  __shared__ int tile_info[3];
+  __shared__ int tile_info[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -156,8 +166,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     mt = first + r % gsz;
     nt = r / gsz;
   } else {
-    nt = t / p.MT;  // m-tiles of one n-panel are consecutive: the expert's B panel stays in L2
-    mt = t % p.MT;
+    // Expert-major order: the m-tiles of all experts are concatenated and tile
+    // t belongs to m-tile t / NT's expert; that expert's mt_g x NT tiles are
+    // consecutive in t (n-tile major), so one XCD works through one expert at
+    // a time and its weight panel and token rows are each fetched about once.
+    mt = t / p.NT;
+    nt = 0;
   }
 
   int64_t row_lo, row_hi;
@@ -168,7 +182,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     row_hi = row_lo + BM < p.M ? row_lo + BM : p.M;
   } else {
     if (wave == 0) {
-      int running = 0, found = -1, f_lo = 0, f_hi = 0;
+      int running = 0, found = -1, f_lo = 0, f_hi = 0, f_nt = 0;
       const int64_t Mt = p.M;
       for (int64_t base = 0; base < p.G; base += 64) {
         const int64_t g = base + lane;
@@ -191,11 +205,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
         const unsigned long long who = __ballot(mine);
         if (who) {
           const int src = __ffsll(who) - 1;
-          const int64_t my_lo = lo + static_cast<int64_t>(mt - excl) * BM;
-          const int64_t my_hi = my_lo + BM < hi ? my_lo + BM : hi;
+          const int g_excl = __shfl(excl, src);
+          const int g_cnt = __shfl(cnt, src);
+          const int g_lo = __shfl(static_cast<int>(lo), src);
+          const int g_hi = __shfl(static_cast<int>(hi), src);
+          const int local = t - g_excl * p.NT;
+          f_nt = local / g_cnt;
+          f_lo = g_lo + (local % g_cnt) * BM;
+          f_hi = f_lo + BM < g_hi ? f_lo + BM : g_hi;
           found = __shfl(static_cast<int>(g), src);
-          f_lo = __shfl(static_cast<int>(my_lo), src);
-          f_hi = __shfl(static_cast<int>(my_hi), src);
           break;
         }
         running += __shfl(incl, 63);
@@ -205,6 +223,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
         tile_info[0] = found;
         tile_info[1] = f_lo;
         tile_info[2] = f_hi;
+        tile_info[3] = f_nt;
       }
     }
     __syncthreads();
@@ -212,6 +231,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     if (g < 0) return;  // whole workgroup
     row_lo = tile_info[1];
     row_hi = tile_info[2];
+    nt = tile_info[3];
     bmat += static_cast<int64_t>(g) * p.N * p.K;
     bscale += static_cast<int64_t>(g) * (p.N / 128) * p.KB;
   }
@@ -226,17 +246,19 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // slot, so every wavefront issues exactly LOADS loads per stage.
   const int lrow = lane >> 3;
   const int lchunk = ((lane & 7) ^ lrow) * 16;
-  const uint8_t* ga[A_DMA];
-  const uint8_t* gb[B_DMA];
+  // Byte offsets within the tile's row panels (below 256 * K < 2^32).
+  const uint8_t* a_base = uniform_ptr(p.a + row_lo * p.K);
+  const uint8_t* b_base = uniform_ptr(bmat + n0 * p.K);
+  uint32_t va[A_DMA], vb[B_DMA];
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
     const int r = wave * (BM / 8) + i * 8 + lrow;
     int64_t row = row_lo + r;
     row = row < row_hi ? row : row_hi - 1;
-    ga[i] = p.a + row * p.K + lchunk;
+    va[i] = static_cast<uint32_t>((row - row_lo) * p.K + lchunk);
   }
 #pragma unroll
-  for (int i = 0; i < B_DMA; ++i) gb[i] = bmat + (n0 + wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk;
+  for (int i = 0; i < B_DMA; ++i) vb[i] = static_cast<uint32_t>((wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk);
   const float* gs;
   if (wave < SA_WAVES) {
     int64_t row = row_lo + wave * 64 + lane;
@@ -255,14 +277,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (uwave == SA_WAVES ? 64 * 4 : 0);
 
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
-  constexpr int SPREAD = SN >= 4 ? SN / 2 : SN;  // sub-tile steps that issue them
+  constexpr int SPREAD = SN >= 8 ? 6 : (SN >= 4 ? SN / 2 : SN);  // sub-tile steps that issue them
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
     if (d < A_DMA)
-      dma16(ga[d] + kof, lds_ta + so + d * 1024);
+      dma16(a_base + kof, va[d], lds_ta + so + d * 1024);
     else
-      dma16(gb[d - A_DMA] + kof, lds_tb + so + (d - A_DMA) * 1024);
+      dma16(b_base + kof, vb[d - A_DMA], lds_tb + so + (d - A_DMA) * 1024);
   };
   auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
   auto issue = [&](int kb, int st) {
@@ -324,7 +346,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 #pragma unroll
         for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
       }
-      if (i == 0) dma_scale(kb_fill, st_fill);
+      if (i == 0) {
+        // With two stages every wait drains all loads, so the filler DMAs that
+        // keep the per-wavefront load count uniform are only needed with more.
+        if (STAGES > 2 || uwave <= SA_WAVES) dma_scale(kb_fill, st_fill);
+      }
       const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
 #pragma unroll
       for (int j = 0; j < SM; ++j) {
@@ -445,7 +471,8 @@ hipError_t launch_any(const GemmArgs& g, bool grouped, hipStream_t s) {
 }  // namespace
 
 bool fp8_block_kernel_applies(const GemmArgs& g) {
-  return !g.exact && !g.row_scales && g.N % 256 == 0;
+  // (the DMA lane offsets are 32-bit: 256 rows x K bytes must stay below 4 GiB)
+  return !g.exact && !g.row_scales && g.N % 256 == 0 && g.K < (int64_t(1) << 24);
 }
 
 // Dense GEMMs use the 256 x 256 tile (least L2 traffic per flop).  Grouped
