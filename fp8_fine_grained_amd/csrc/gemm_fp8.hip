@@ -14,10 +14,11 @@
 //    (128-row tiles waste less of the last tile of each ~256-row expert segment).
 //    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
 //  * One 128-wide K block per LDS stage; the loads of block kb+STAGES-1 are in
-//    flight while block kb is multiplied.  They are issued over the first half
-//    of the sub-tile steps (a few DMAs per step, between MFMAs): early enough to
-//    land before the end of the iteration, spread enough that no wavefront
-//    stalls on a full memory-instruction queue before its first MFMAs.
+//    flight while block kb is multiplied.  They are issued over the first six
+//    of the eight sub-tile steps (first two of four for 128 x 256), one or two
+//    DMAs per step between MFMAs: early enough to land before the end of the
+//    iteration, spread out because each DMA costs the issuing wavefront and the
+//    LDS both per instruction and per byte.
 //  * Tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    issued through inline assembly together with the waits and barriers: the
 //    compiler cannot tell that an LDS read does not overlap the DMA writes still
@@ -38,7 +39,8 @@
 //    are being read.
 //  * Dense tiles are numbered so that each XCD (workgroup id mod 8) works on one
 //    contiguous band of the tile grid, keeping its operand panels in its L2;
-//    grouped tiles put the m-tiles of one (expert, n-tile) next to each other.
+//    grouped tiles are in expert-major order, so one XCD works through one
+//    expert's tiles at a time.
 #include "launch.h"
 
 namespace fp8fg {

@@ -2,7 +2,7 @@
 
 Usage (from the repository root, after copying rocprofv3 output back):
 
-    python -m fp8_fine_grained_amd.profile_summary stats <kernel_stats.csv> <out.md> "<command>"
+    python -m fp8_fine_grained_amd.profile_summary stats <kernel_stats.csv> <out.md> "<command>" [bench.log]
     python -m fp8_fine_grained_amd.profile_summary traffic <fetch.csv> <write.csv> \
         <calib_fetch.csv> <calib_write.csv> <kernel-substring> <kernel-source> <out.md> \
         "<fetch command>" "<write command>" "<calibration commands>"
@@ -17,6 +17,7 @@ The summary records the sha256 of the kernel source it was measured with;
 
 import csv
 import hashlib
+import os
 import json
 import sys
 
@@ -28,7 +29,19 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def stats(csv_path, out_md, command):
+def _bench_line(log_path):
+    """The JSON line bench.py printed in the profiled run (None if absent)."""
+    try:
+        lines = open(log_path).read().splitlines()
+    except OSError:
+        return None
+    for line in reversed(lines):
+        if line.startswith("{") and '"metric"' in line:
+            return json.loads(line)
+    return None
+
+
+def stats(csv_path, out_md, command, bench_log=None):
     rows = _rows(csv_path)
     lines = [
         "# rocprofv3 kernel statistics",
@@ -49,6 +62,27 @@ def stats(csv_path, out_md, command):
         lines.append(
             f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    bench = _bench_line(bench_log) if bench_log else None
+    trace = os.path.join(os.path.dirname(csv_path), os.path.basename(csv_path).replace("kernel_stats", "kernel_trace"))
+    if bench and os.path.exists(trace):
+        # the timed launches are each kernel's last `steps` dispatches
+        n = int(bench["steps"])
+        durs = {}
+        for r in _rows(trace):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", f"rocprofv3 average over each kernel's last {n} dispatches (the timed steps):", "",
+                  "| kernel | dispatches | average (us) |", "|---|---|---|"]
+        for name, d in durs.items():
+            d = [x for _, x in sorted(d)][-n:]
+            short = name if len(name) <= 110 else name[:107] + "..."
+            lines.append(f"| `{short}` | {len(d)} | {sum(d) / len(d) / 1e3:.2f} |")
+    if bench:
+        lines += ["", "bench.py's own HIP-event averages over the same timed steps (the first table also",
+                  "counts the warm-up launches):", "", "| launch | ms |", "|---|---|"]
+        for name, k in bench.get("kernels", {}).items():
+            lines.append(f"| {name} | {k['ms']:.4f} |")
+        lines.append(f"| whole step | {bench['ms_per_step']:.4f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -137,7 +171,7 @@ def load_traffic(md_path):
 
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
-        stats(*sys.argv[2:5])
+        stats(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:12])
     else:
