@@ -98,6 +98,21 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row0, int lane) {
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
 }
+// The same with only the lanes of `mask` active.  The instruction is always
+// issued (no branch around it), so every wavefront's count of outstanding
+// loads per stage stays the same whatever the mask.
+__device__ __forceinline__ void dma16_masked(const uint8_t* base, uint32_t voff, uint32_t lds, uint64_t mask) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(base), "s"(mask)
+      : "memory");
+}
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
 }
@@ -252,10 +267,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   const uint8_t* a_base = uniform_ptr(p.a + row_lo * p.K);
   const uint8_t* b_base = uniform_ptr(bmat + n0 * p.K);
   uint32_t va[A_DMA], vb[B_DMA];
+  uint64_t a_live[A_DMA];  // grouped: lanes whose tile row lies inside the segment
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
     const int r = wave * (BM / 8) + i * 8 + lrow;
     int64_t row = row_lo + r;
+    a_live[i] = __ballot(row < row_hi);
     row = row < row_hi ? row : row_hi - 1;
     va[i] = static_cast<uint32_t>((row - row_lo) * p.K + lchunk);
   }
@@ -283,8 +300,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
-    if (d < A_DMA)
-      dma16(a_base + kof, va[d], lds_ta + so + d * 1024);
+    if (d < A_DMA) {
+      if constexpr (GROUPED)
+        dma16_masked(a_base + kof, va[d], lds_ta + so + d * 1024, a_live[d]);
+      else
+        dma16(a_base + kof, va[d], lds_ta + so + d * 1024);
+    }
     else
       dma16(b_base + kof, vb[d - A_DMA], lds_tb + so + (d - A_DMA) * 1024);
   };
@@ -303,6 +324,21 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 
   const int KB = p.KB;
   auto clampkb = [&](int kb) { return kb < KB ? kb : KB - 1; };
+  if constexpr (GROUPED) {
+    // Rows past the end of the expert's segment are never loaded: their LDS
+    // slots are zeroed once here, so their MFMAs multiply zeros (which costs the
+    // matrix cores far less power than the clamped copies of a real row would)
+    // and their outputs, never stored, are zero.
+#pragma unroll
+    for (int i = 0; i < A_DMA; ++i) {
+      if (!((a_live[i] >> lane) & 1)) {
+#pragma unroll
+        for (int s0 = 0; s0 < STAGES; ++s0)
+          *reinterpret_cast<u32x4*>(tiles + s0 * STAGE + (wave * (BM / 8) + i * 8) * 128 + lane * 16) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
   // prologue: blocks 0 .. STAGES-2 into stages 0 .. STAGES-2
 #pragma unroll
   for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(clampkb(s0), s0);
