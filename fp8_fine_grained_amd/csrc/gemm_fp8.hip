@@ -50,6 +50,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int NTHREADS = 512;  // 8 wavefronts, 2 per SIMD
@@ -87,6 +89,32 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row0, int lane) {
   f[0] = c0[0]; f[1] = c0[1]; f[2] = c0[2]; f[3] = c0[3];
   f[4] = c1[0]; f[5] = c1[1]; f[6] = c1[2]; f[7] = c1[3];
   return f;
+}
+
+// Exact widening of 8 E4M3 codes (two dwords) to fp16: every E4M3 value,
+// subnormals included, is an fp16 value.
+__device__ __forceinline__ v8h widen8(uint32_t lo, uint32_t hi) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(lo), 1.0f, false);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(lo), 1.0f, true);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(hi), 1.0f, false);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(hi), 1.0f, true);
+  v8h r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// A fragment widened for four 16x16x32 fp16 MFMAs: part q holds the lane's
+// bytes 8q .. 8q+7 of its 32, so across the four lane groups part q covers 32
+// of the 128 K values, and A and B are split the same way.
+struct WideFrag {
+  v8h q[4];
+};
+__device__ __forceinline__ WideFrag widen(const v8i& f) {
+  WideFrag w;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w.q[q] = widen8(static_cast<uint32_t>(f[2 * q]), static_cast<uint32_t>(f[2 * q + 1]));
+  return w;
 }
 
 // LDS DMA: 64 lanes x 16 bytes (or 4 bytes) to 1 KB (256 B) of LDS starting
@@ -138,22 +166,28 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // BM x BN output tile (m x n), WM x WN wavefronts, STAGES K blocks in LDS.
-template <int BM, int BN, int WM, int WN, int STAGES, bool BF16OUT, bool GROUPED>
+// EXACT: operands widened to fp16 and multiplied by fp16 MFMAs (every product and
+// every in-instruction sum exact); ROWS: one weight-side scale per row n and
+// K block instead of one per 128 x 128 block.
+template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) {
   static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
   constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
   constexpr int SM = TM / 16, SN = TN / 16;
-  static_assert(TN % 128 == 0 || 128 % TN == 0, "a wavefront's n range lies in one weight block");
+  static_assert(ROWS || TN % 128 == 0 || 128 % TN == 0, "a wavefront's n range lies in one weight block");
   constexpr int TILE_A = BM * 128;
   constexpr int TILE_B = BN * 128;
   constexpr int STAGE = TILE_A + TILE_B;
   constexpr int A_DMA = BM / 64, B_DMA = BN / 64;  // 8-row DMAs per wavefront per stage
-  constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales
-  static_assert(SA_WAVES < 8, "one wavefront left for the weight-block scales");
+  constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales (64 rows each)
+  constexpr int SB_WAVES = ROWS ? BN / 64 : 1;       // and the B scales (64 rows, or all blocks)
+  static_assert(SA_WAVES + SB_WAVES <= 8, "one scale DMA per wavefront");
+  constexpr int SB_LEN = ROWS ? BN : 64;
   // loads per wavefront per stage: tiles + one scale (or filler) DMA
   constexpr int LOADS = A_DMA + B_DMA + 1;
   constexpr int WAIT_N = (STAGES - 2) * LOADS;
   static_assert(STAGES >= 2, "at least double buffering");
+  static_assert(!(ROWS && GROUPED), "grouped weights carry block scales");
   // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
   // padded by 16) in its own slice of the tile buffer.
   constexpr int EPI_PITCH = TN * 2 + 16;
@@ -161,7 +195,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   constexpr int TILES_BYTES = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[TILES_BYTES];
   __shared__ __attribute__((aligned(16))) float s_sa[STAGES][BM];
-  __shared__ __attribute__((aligned(16))) float s_sb[STAGES][64];
+  __shared__ __attribute__((aligned(16))) float s_sb[STAGES][SB_LEN];
   __shared__ __attribute__((aligned(16))) float s_filler[64];  // landing slot of the filler DMAs, never read
   __shared__ int tile_info[4];
 
@@ -283,6 +317,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     int64_t row = row_lo + wave * 64 + lane;
     row = row < row_hi ? row : row_hi - 1;
     gs = p.sa + row * p.KB;
+  } else if constexpr (ROWS) {
+    int w = wave - SA_WAVES;
+    w = w < SB_WAVES ? w : 0;  // filler wavefronts re-read the first weight rows' scales
+    gs = bscale + (n0 + w * 64 + lane) * p.KB;
   } else {
     const int blk = lane < BN / 128 - 1 ? lane : BN / 128 - 1;
     gs = bscale + (n0 / 128 + blk) * p.KB;
@@ -291,9 +329,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / 8) * 128;
   const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (BN / 8) * 128;
+  const bool b_scale_wave = uwave >= SA_WAVES && uwave < SA_WAVES + SB_WAVES;
   const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
-                                           : (uwave == SA_WAVES ? lds_addr(&s_sb[0][0]) : lds_addr(s_filler));
-  const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (uwave == SA_WAVES ? 64 * 4 : 0);
+                          : (b_scale_wave ? lds_addr(&s_sb[0][(uwave - SA_WAVES) * 64]) : lds_addr(s_filler));
+  const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (b_scale_wave ? SB_LEN * 4 : 0);
 
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
   constexpr int SPREAD = SN >= 8 ? 6 : (SN >= 4 ? SN / 2 : SN);  // sub-tile steps that issue them
@@ -345,26 +384,64 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   wait_barrier<WAIT_N>();  // block 0 resident
 
   // Fragments of the current block: all m sub-tiles, the first n sub-tile, and
-  // the per-column promotion factors sa[m,kb] * sb[nb,kb] (block 0 here; the
-  // loop requests each next block's right after its barrier).
+  // the per-column promotion factors sa[m,kb] * sb[nb,kb] (block mode) or sa[m,kb]
+  // (row mode, where sb[n,kb] is read per n sub-tile); block 0 here, and the
+  // loop requests each next block's right after its barrier.
   v8i fm[SM];
   float f[SM];
   v8i fn;
-  auto load_frags = [&](int st) {
-    const uint8_t* tA = tiles + st * STAGE;
-    const uint8_t* tB = tA + TILE_A;
-    const float sbv = s_sb[st][(wn * TN) / 128];
+  auto factor = [&](int st, int j) {
+    const float a = s_sa[st][wm * TM + j * 16 + (lane & 15)];
+    if constexpr (ROWS)
+      return a;
+    else
+      return a * s_sb[st][(wn * TN) / 128];
+  };
+  // Row mode: the 4 weight-row scales of this lane in n sub-tile i.
+  auto row_scales = [&](int st, int i) {
+    return *reinterpret_cast<const v4f*>(&s_sb[st][(wn * TN + i * 16 + 4 * (lane >> 4)) % SB_LEN]);
+  };
+  {
+    const uint8_t* tA = tiles;
 #pragma unroll
     for (int j = 0; j < SM; ++j) {
       fm[j] = frag(tA, wm * TM + j * 16, lane);
-      f[j] = s_sa[st][wm * TM + j * 16 + (lane & 15)] * sbv;
+      f[j] = factor(0, j);
     }
-    fn = frag(tB, wn * TN, lane);
+    fn = frag(tA + TILE_A, wn * TN, lane);
+  }
+
+  // 128-K partial of n sub-tile `b` and m sub-tile `a` (MFMA A = weight rows).
+  WideFrag wm_frag[EXACT ? SM : 1];
+  auto partial = [&](const v8i& b, const WideFrag& wb, int j) {
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!EXACT) {
+      (void)wb;
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, fm[j], z, 0, 0, 0, 0, 0, 0);
+    } else {
+      (void)b;
+      v4f r = z;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb.q[q], wm_frag[j].q[q], r, 0, 0, 0);
+      return r;
+    }
   };
-  load_frags(0);
+  // acc[i] += P * factor, with the row scales of sub-tile i in row mode.
+  auto promote = [&](v4f (&a)[SM], const v4f (&P)[SM], const float (&fv)[SM], const v4f& sbr) {
+#pragma unroll
+    for (int j = 0; j < SM; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (ROWS)
+          a[j][r] = fmaf(P[j][r] * sbr[r], fv[j], a[j][r]);
+        else
+          a[j][r] = fmaf(P[j][r], fv[j], a[j][r]);
+      }
+  };
 
   int st = 0;  // stage holding block kb
   v4f P[2][SM];
+  v4f sbr[2];  // row mode: row scales of the sub-tiles whose partials are pending
   for (int kb = 0; kb < KB; ++kb) {
     // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
     // Near the end the free stage is refilled with block KB-1, which is not read
@@ -372,6 +449,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     const int st_fill = st == 0 ? STAGES - 1 : st - 1;
     const int kb_fill = clampkb(kb + STAGES - 1);
     const uint8_t* tB = tiles + st * STAGE + TILE_A;
+    if constexpr (EXACT) {
+#pragma unroll
+      for (int j = 0; j < SM; ++j) wm_frag[j] = widen(fm[j]);
+    }
     __builtin_amdgcn_s_setprio(1);  // the issuing phase of the matrix cores goes first
     // Sub-tile steps 0 .. SN-2: the fragment of step i+1 is read from LDS while
     // the MFMAs of step i run, and the promotion FMAs of step i-1 (double-
@@ -387,22 +468,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       if (i == 0) {
         // With two stages every wait drains all loads, so the filler DMAs that
         // keep the per-wavefront load count uniform are only needed with more.
-        if (STAGES > 2 || uwave <= SA_WAVES) dma_scale(kb_fill, st_fill);
+        if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
       }
       const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
+      if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
+      WideFrag wn_frag;
+      if constexpr (EXACT) wn_frag = widen(fn);
 #pragma unroll
-      for (int j = 0; j < SM; ++j) {
-        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-        P[i & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fn, fm[j], z, 0, 0, 0, 0, 0, 0);
-      }
-      if (i > 0) {
-#pragma unroll
-        for (int j = 0; j < SM; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = fmaf(P[(i - 1) & 1][j][r], f[j], acc[i - 1][j][r]);
-      }
+      for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
+      if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1]);
       fn = fn_next;
     }
+    if constexpr (ROWS) sbr[(SN - 1) & 1] = row_scales(st, SN - 1);
 
     // Every LDS read of this stage has been issued: once they have returned and
     // block kb+1 is resident, the workgroup synchronises.  The last step's MFMAs
@@ -416,25 +493,19 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     for (int j = 0; j < SM; ++j) f_old[j] = f[j];
     {
       const uint8_t* tA = tiles + st * STAGE;
-      const float sbv = s_sb[st][(wn * TN) / 128];
+      WideFrag wn_frag;
+      if constexpr (EXACT) wn_frag = widen(fn);
 #pragma unroll
       for (int j = 0; j < SM; ++j) {
-        const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-        P[(SN - 1) & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fn, fm[j], z, 0, 0, 0, 0, 0, 0);
+        P[(SN - 1) & 1][j] = partial(fn, wn_frag, j);
         // (After the final block this reads a stage nobody uses; the values are dropped.)
         fm[j] = frag(tA, wm * TM + j * 16, lane);
-        f[j] = s_sa[st][wm * TM + j * 16 + (lane & 15)] * sbv;
+        f[j] = factor(st, j);
       }
       fn = frag(tA + TILE_A, wn * TN, lane);
     }
-#pragma unroll
-    for (int j = 0; j < SM; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[SN - 2][j][r] = fmaf(P[(SN - 2) & 1][j][r], f_old[j], acc[SN - 2][j][r]);
-#pragma unroll
-    for (int j = 0; j < SM; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_old[j], acc[SN - 1][j][r]);
+    promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1]);
+    promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1]);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
@@ -488,36 +559,41 @@ template <int CFG> struct Cfg;
 template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
 
-template <int CFG, bool BF16OUT, bool GROUPED>
+template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using C = Cfg<CFG>;
   const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
   FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.M, g.N, g.K, g.G,
             static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN)};
   const unsigned blocks = static_cast<unsigned>(MT * p.NT);
-  hipLaunchKernelGGL((gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, BF16OUT, GROUPED>), dim3(blocks),
-                     dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL((gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED>),
+                     dim3(blocks), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
-template <int CFG>
-hipError_t launch_any(const GemmArgs& g, bool grouped, hipStream_t s) {
-  if (grouped) return g.y_bf16 ? launch_cfg<CFG, true, true>(g, s) : launch_cfg<CFG, false, true>(g, s);
-  return g.y_bf16 ? launch_cfg<CFG, true, false>(g, s) : launch_cfg<CFG, false, false>(g, s);
+template <int CFG, bool EXACT, bool ROWS, bool GROUPED>
+hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
+  return g.y_bf16 ? launch_cfg<CFG, EXACT, ROWS, true, GROUPED>(g, s) : launch_cfg<CFG, EXACT, ROWS, false, GROUPED>(g, s);
 }
 
 }  // namespace
 
 bool fp8_block_kernel_applies(const GemmArgs& g) {
   // (the DMA lane offsets are 32-bit: 256 rows x K bytes must stay below 4 GiB)
-  return !g.exact && !g.row_scales && g.N % 256 == 0 && g.K < (int64_t(1) << 24);
+  return g.N % 256 == 0 && g.K < (int64_t(1) << 24);
 }
 
-// Dense GEMMs use the 256 x 256 tile (least L2 traffic per flop).  Grouped
-// GEMMs use 128-row tiles: expert segments of ~256 rows then waste less of the
-// last m-tile of each segment, and the third stage hides the weight streaming.
+// Block-scaled FP8 accumulation: dense GEMMs use the 256 x 256 tile (least L2
+// and LDS traffic per flop), grouped GEMMs the 128-row tile (expert segments of
+// ~256 rows then waste less of their last m-tile).  The exact mode (fp16
+// operands, twice the fragment registers) and the row-scaled mode (one more
+// multiply and four row scales per sub-tile) use the 64 x 64 wavefront tile.
 hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s) {
-  return grouped ? launch_any<1>(g, true, s) : launch_any<0>(g, false, s);
+  if (grouped)
+    return g.exact ? launch_out<1, true, false, true>(g, s) : launch_out<1, false, false, true>(g, s);
+  if (g.exact)
+    return g.row_scales ? launch_out<1, true, true, false>(g, s) : launch_out<1, true, false, false>(g, s);
+  return g.row_scales ? launch_out<1, false, true, false>(g, s) : launch_out<0, false, false, false>(g, s);
 }
 
 }  // namespace fp8fg
