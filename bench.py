@@ -11,10 +11,10 @@ events on its stream, and the quantisers are timed afterwards as batches.  The t
 inputs are rotated over three HBM copies so that the 256 MB last-level cache
 cannot serve the quantisers' reads from one step to the next.
 
-Other workloads (``--workload quant|moe|wgrad``) measure the remaining rows of
+Other workloads (``--workload quant|moe|wgrad|dgrad``) measure the remaining rows of
 the path and print their own JSON line; the default run prints exactly one line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad]
                     [--no-cpu-baseline]
 """
 
@@ -400,6 +400,70 @@ def bench_wgrad(args, torch, fp8, workloads):
     }
 
 
+def bench_dgrad(args, torch, fp8, workloads):
+    # dX [M,K] = dY [M,N] W [N,K]: dY quantised 1x128 along N, W quantised 128x128
+    # once for both orientations, the GEMM reads the transposed codes.
+    M, N, K = 4096, 7168, 7168
+    d = workloads.dgrad()
+    dys = [d["dy"].cuda() for _ in range(3)]
+    ws = [d["w"].cuda() for _ in range(3)]
+    qa = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, N // 128), dtype=torch.float32, device="cuda")
+    q = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    s = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    qt = torch.empty((K, N), dtype=torch.uint8, device="cuda")
+    st = torch.empty((K // 128, N // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    t_gemm = Timer(torch, args.steps)
+    t_act, t_w = Timer(torch, 1), Timer(torch, 1)
+
+    def step(i, timed):
+        fp8.fp8_quant_act_1x128(dys[i % 3], qa, sa)
+        fp8.fp8_quant_weight_128x128_dual(ws[i % 3], q, s, qt, st)
+        if timed:
+            with t_gemm:
+                fp8.fp8_block_gemm(qa, sa, qt, st, accum="fp8", y=y)
+        else:
+            fp8.fp8_block_gemm(qa, sa, qt, st, accum="fp8", y=y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    with t_act:
+        for i in range(args.steps):
+            fp8.fp8_quant_act_1x128(dys[i % 3], qa, sa)
+    with t_w:
+        for i in range(args.steps):
+            fp8.fp8_quant_weight_128x128_dual(ws[i % 3], q, s, qt, st)
+    torch.cuda.synchronize()
+    flop = 2.0 * M * N * K
+    gms = t_gemm.mean_ms()
+    act_bytes = M * N * 3 + M * (N // 128) * 4
+    dual_bytes = N * K * 4 + 2 * (N // 128) * (K // 128) * 4
+    return {
+        "metric": "data-gradient FP8 GEMM TFLOP/s", "value": flop / dt / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "data gradient dX = dY W of the dense projection: dY bf16 [4096,7168] ~ N(0,1e-3) "
+                               "quantised 1x128, W bf16 [7168,7168] quantised 128x128 with the transposed codes "
+                               "written in the same pass, block-scaled GEMM on W^T, bf16 out",
+                   "M": M, "N": K, "K": N, "input_copies_rotated": 3},
+        "kernels": {
+            "fp8_quant_act_1x128": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
+            "fp8_quant_weight_128x128_dual": _hbm_line("dual", t_w.mean_ms() / args.steps, dual_bytes, {}),
+            "fp8_block_gemm": {"ms": gms, "TFLOP/s": flop / (gms * 1e-3) / 1e12,
+                               "frac_fp8_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
+        },
+        "roofline": {"bound": "mfma", "achieved": flop / (gms * 1e-3) / 1e12, "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flop / (gms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, "traffic": None},
+    }
+
+
 def copy_calibration(args, torch):
     """A plain 1 GiB device-to-device copy: the reference for scaling rocprofv3 byte counters."""
     n = 1 << 30
@@ -416,7 +480,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -436,7 +500,8 @@ def main():
     import fp8_fine_grained_amd.binding as fp8
     from fp8_fine_grained_amd import workloads
 
-    fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad}[args.workload]
+    fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
+          "dgrad": bench_dgrad}[args.workload]
     out = fn(args, torch, fp8, workloads)
     print(json.dumps(out), flush=True)
 

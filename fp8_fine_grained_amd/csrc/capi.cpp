@@ -75,6 +75,22 @@ int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, i
                                                static_cast<hipStream_t>(stream)));
 }
 
+int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
+                                  fp8fg_stream_t stream) {
+  if (!valid_dtype(w_dtype) || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return FP8FG_OK;
+  if (N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!w || !q || !scales || !q_t || !scales_t) return FP8FG_ERR_INVALID_ARG;
+  if (ld_w < K) return FP8FG_ERR_INVALID_ARG;
+  if ((N / 128) * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (!aligned(w, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(scales, 4) || !aligned(scales_t, 4) ||
+      (ld_w * elem_size(w_dtype)) % 16 != 0)
+    return FP8FG_ERR_MISALIGNED;
+  return hip_status(fp8fg::launch_quant_weight_dual(w, w_dtype == FP8FG_BF16, N, K, ld_w, q, scales, q_t, scales_t,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,

@@ -16,6 +16,9 @@ hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K,
 // 128x128 quantisation.
 hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
                                uint8_t* q, float* scales, hipStream_t s);
+// 128x128 quantisation writing q [N,K] and the transposed q_t [K,N] (+ scales, scales_t).
+hipError_t launch_quant_weight_dual(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+                                    uint8_t* q, float* scales, uint8_t* qt, float* scales_t, hipStream_t s);
 
 struct GemmArgs {
   const uint8_t* a;

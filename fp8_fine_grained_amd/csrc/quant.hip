@@ -269,6 +269,112 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const void* __restric
   if (threadIdx.x == 0) scales[blockIdx.x] = s;
 }
 
+// 4 x 4 byte transpose: t[e] byte r = byte e of r4[r].
+__device__ __forceinline__ void transpose4x4(const uint32_t (&r4)[4], uint32_t (&t)[4]) {
+  const uint32_t x0 = __builtin_amdgcn_perm(r4[1], r4[0], 0x05010400u);  // r0.b0 r1.b0 r0.b1 r1.b1
+  const uint32_t x1 = __builtin_amdgcn_perm(r4[1], r4[0], 0x07030602u);  // r0.b2 r1.b2 r0.b3 r1.b3
+  const uint32_t y0 = __builtin_amdgcn_perm(r4[3], r4[2], 0x05010400u);
+  const uint32_t y1 = __builtin_amdgcn_perm(r4[3], r4[2], 0x07030602u);
+  t[0] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
+  t[1] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
+  t[2] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+  t[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+}
+
+// 128x128 quantisation that writes the codes twice: row-major q [N,K] and
+// transposed q_t [K,N].  The blocks of W^T are the transposes of the blocks of
+// W with the same amax, so q_t and scales_t (= scales transposed) are exactly
+// the 128x128 quantisation of W^T: the B operand of the data-gradient GEMM.
+// Thread (q4, cg) holds rows 4*q4 .. 4*q4+3 and columns 16*cg .. 16*cg+15 of
+// the block; it writes 16 row-major code runs of 4 bytes (after a 4x4 byte
+// transpose) into an LDS tile of the transposed block, whose 32-dword rows are
+// XOR-permuted by ((row >> 4) & 3) << 3 (two lanes per bank at most), and the
+// tile leaves as full 128-byte rows.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __restrict__ w, int64_t ld, int GK, int GN,
+                                                                uint8_t* __restrict__ q, float* __restrict__ scales,
+                                                                uint8_t* __restrict__ qt, float* __restrict__ scales_t,
+                                                                int64_t N, int64_t K) {
+  __shared__ float wave_max[4];
+  __shared__ __attribute__((aligned(16))) uint32_t tr[128 * 32];
+  const int bi = blockIdx.x / GK;
+  const int bj = blockIdx.x - bi * GK;
+  const int cg = threadIdx.x & 7;
+  const int q4 = threadIdx.x >> 3;
+  constexpr int ES = BF16 ? 2 : 4;
+  float v[4][16];
+  float amax = 0.0f;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int64_t row = static_cast<int64_t>(bi) * 128 + 4 * q4 + rr;
+    const char* src = static_cast<const char*>(w) + (row * ld + static_cast<int64_t>(bj) * 128 + cg * 16) * ES;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + h);
+        const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[rr][8 * h + 2 * j] = bf16_lo(wd[j]);
+          v[rr][8 * h + 2 * j + 1] = bf16_hi(wd[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const f32x4 f = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + h);
+        v[rr][4 * h] = f.x; v[rr][4 * h + 1] = f.y; v[rr][4 * h + 2] = f.z; v[rr][4 * h + 3] = f.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[rr][e]));
+  amax = max64(amax);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  float s, inv;
+  group_scale(amax, s, inv);
+  uint32_t codes[4][4];  // [row rr][dword d]: columns 4d .. 4d+3 of the thread's 16
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int64_t row = static_cast<int64_t>(bi) * 128 + 4 * q4 + rr;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      codes[rr][d] = cvt4(v[rr][4 * d] * inv, v[rr][4 * d + 1] * inv, v[rr][4 * d + 2] * inv, v[rr][4 * d + 3] * inv);
+    __builtin_nontemporal_store(u32x4{codes[rr][0], codes[rr][1], codes[rr][2], codes[rr][3]},
+                                reinterpret_cast<u32x4*>(q + row * K + static_cast<int64_t>(bj) * 128 + cg * 16));
+  }
+  // Transposed tile: row c = column of the block (a K index), dword q4 = its 4
+  // codes of rows 4*q4 .. 4*q4+3.
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t r4[4] = {codes[0][d], codes[1][d], codes[2][d], codes[3][d]};
+    uint32_t t[4];
+    transpose4x4(r4, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = cg * 16 + 4 * d + e;
+      tr[c * 32 + (q4 ^ (((c >> 4) & 3) << 3))] = t[e];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int idx = threadIdx.x + 256 * t;
+    const int c = idx >> 3, ch = idx & 7;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&tr[c * 32 + 4 * (ch ^ (((c >> 4) & 3) << 1))]);
+    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(qt + (static_cast<int64_t>(bj) * 128 + c) * N +
+                                                              static_cast<int64_t>(bi) * 128 + ch * 16));
+  }
+  if (threadIdx.x == 0) {
+    scales[blockIdx.x] = s;
+    scales_t[static_cast<int64_t>(bj) * GN + bi] = s;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
@@ -304,6 +410,19 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, i
     hipLaunchKernelGGL(quant_weight_kernel<true>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
   else
     hipLaunchKernelGGL(quant_weight_kernel<false>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_dual(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+                                    uint8_t* q, float* scales, uint8_t* qt, float* scales_t, hipStream_t s) {
+  const int GK = static_cast<int>(K / 128), GN = static_cast<int>(N / 128);
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(GN) * GK));
+  if (bf16)
+    hipLaunchKernelGGL(quant_weight_dual_kernel<true>, grid, dim3(256), 0, s, w, ld, GK, GN, q, scales, qt, scales_t,
+                       N, K);
+  else
+    hipLaunchKernelGGL(quant_weight_dual_kernel<false>, grid, dim3(256), 0, s, w, ld, GK, GN, q, scales, qt,
+                       scales_t, N, K);
   return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ bfloat16 with round-to-nearest-even where the workload is bf16):
                 65536 permuted rows and 257 segment offsets; expert weights
                 bf16 [2048,7168] ~ N(0, 0.02), drawn per expert on demand.
 * ``wgrad``     dY bf16 [16384,7168] ~ N(0, 1e-3); X bf16 [16384,7168] ~ N(0,1).
+* ``dgrad``     dY bf16 [4096,7168] ~ N(0, 1e-3); W bf16 [7168,7168] ~ N(0, 0.02)
+                (the data gradient dX = dY W of the dense projection).
 
 N(mu, sigma) names the standard deviation.  Outliers: exactly
 floor(p * numel) positions drawn without replacement, multiplied by the
@@ -162,6 +164,13 @@ def wgrad(seed=5, T=16384, C=7168, Cin=None):
     dy = _draw((T, C), seed, 1, "normal", std=1e-3)
     x = _draw((T, Cin), seed, 2, "normal")
     return {"dy": to_bf16(dy), "x": to_bf16(x)}
+
+
+def dgrad(seed=6, M=4096, N=7168, K=7168):
+    """Data-gradient operands: dY bf16 [M,N] ~ N(0,1e-3), W bf16 [N,K] ~ N(0,0.02)."""
+    dy = _draw((M, N), seed, 1, "normal", std=1e-3)
+    w = _draw((N, K), seed, 2, "normal", std=0.02)
+    return {"dy": to_bf16(dy), "w": to_bf16(w)}
 
 
 def skewed_offsets(M_total, G, big_rows, n_empty, seed=7):

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 1
+#define FP8FG_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum {
@@ -123,6 +123,27 @@ int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_
  */
 int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                              uint8_t* q, float* scales, fp8fg_stream_t stream);
+
+/*
+ * 128x128 weight quantisation that also writes the transposed operand, for the
+ * data-gradient GEMM dX = dY * W (the "transposed read" the tonho.wtf
+ * "DeepSeek-V3" page lists among its hardware wishes, "o que isso custou").
+ * A 128x128 block of W^T is the transpose of a block of W with the same amax,
+ * so the 128x128 quantisation of W^T is exactly the transposed codes with the
+ * transposed scale grid.  Both come from one read of W.
+ *
+ * w, N, K, ld_w, q, scales   as fp8_quant_weight_128x128 (same bytes written).
+ * q_t       out, uint8 codes [K, N] row-major: q_t[k, n] == q[n, k].
+ * scales_t  out, fp32 [K/128, N/128] row-major: scales_t[j, i] == scales[i, j].
+ * With these, fp8_block_gemm(q_dy, s_dy, q_t, scales_t, FP8FG_B_BLOCK_128x128,
+ * ...) computes dX [M, K] = dY [M, N] * W [N, K], where (q_dy, s_dy) is the
+ * 1x128 quantisation of dY along N.
+ * Requirements as fp8_quant_weight_128x128, plus q_t 16-byte aligned and
+ * scales_t 4-byte aligned; no output may alias another.  N == 0 is a no-op.
+ */
+int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
+                                  fp8fg_stream_t stream);
 
 /*
  * Block-scaled FP8 GEMM  Y = deq(A) * deq(B)^T  (innerforce accumulation

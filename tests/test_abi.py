@@ -20,14 +20,15 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
-    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_block_gemm",
-                          "fp8_block_grouped_gemm", "fp8fg_status_string", "fp8fg_abi_version"}
+    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_quant_weight_128x128_dual",
+                          "fp8_block_gemm", "fp8_block_grouped_gemm", "fp8fg_status_string",
+                          "fp8fg_abi_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 1
+    assert L.fp8fg_abi_version() == 2
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -55,6 +56,23 @@ def test_quant_weight_validation(L):
     assert f(GOOD, fp8.F32, 128, 128, 128, NULL, GOOD, NULL) == fp8.ERR_INVALID_ARG
     assert f(GOOD, fp8.F32, 128, 128, 128, GOOD, ctypes.c_void_p(0x10002), NULL) == fp8.ERR_MISALIGNED
     assert f(NULL, fp8.F32, 0, 128, 128, NULL, NULL, NULL) == fp8.OK
+
+
+def test_quant_weight_dual_validation(L):
+    f = L.fp8_quant_weight_128x128_dual
+    ok = dict(w=GOOD, dt=fp8.BF16, N=128, K=256, ld=256, q=GOOD, s=GOOD, qt=GOOD, st=GOOD, stream=NULL)
+    args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
+    assert f(*args(dt=7)) == fp8.ERR_INVALID_ARG
+    assert f(*args(N=-128)) == fp8.ERR_INVALID_ARG
+    assert f(*args(w=NULL, N=0, q=NULL, s=NULL, qt=NULL, st=NULL)) == fp8.OK  # N == 0: no-op
+    assert f(*args(N=100)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(K=200, ld=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(qt=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(st=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(ld=128)) == fp8.ERR_INVALID_ARG  # ld < K
+    assert f(*args(qt=BAD)) == fp8.ERR_MISALIGNED
+    assert f(*args(st=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(ld=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
 
 
 def test_gemm_validation(L):

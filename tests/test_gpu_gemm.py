@@ -93,6 +93,27 @@ def test_wgrad_row_scales_small():
     assert np.all(np.abs(y8 - ref) <= bound)
 
 
+def _dgrad_ops(M, N, K):
+    """dX = dY W: A = dY quantised 1x128 along N, B = (W^T quantised 128x128) from
+    the dual quantiser; the oracle quantises dY and W^T itself."""
+    d = workloads.dgrad(M=M, N=N, K=K)
+    qa, sa = fp8.fp8_quant_act_1x128(d["dy"].cuda())
+    _, _, qt, st = fp8.fp8_quant_weight_128x128_dual(d["w"].cuda())
+    ra, rsa = quant.quant_1x128(f32(d["dy"]))
+    rt, rst = quant.quant_128x128(np.ascontiguousarray(f32(d["w"]).T))
+    assert np.array_equal(qa.cpu().numpy(), ra) and np.array_equal(qt.cpu().numpy(), rt)
+    return (qa, sa, qt, st), (ra, rsa, rt, rst)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 384, 512), (129, 1024, 256)])
+def test_dgrad_small(M, N, K):
+    g, r = _dgrad_ops(M, N, K)
+    ref = gemm.block_gemm(*r)
+    say(f"dgrad dX [{M},{K}] = dY [{M},{N}] W [{N},{K}]")
+    check_bf16(_run(g, M, K, torch.bfloat16, "fp8"), ref, "fp8 accum")
+    check_f32(_run(g, M, K, torch.float32, "exact"), ref, "exact accum fp32")
+
+
 def _sample_rows(M, n, seed):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], rng.choice(M, size=n, replace=False)]))
@@ -130,3 +151,20 @@ def test_full_wgrad():
     assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
     ref = gemm.block_gemm(ra, rsa, rb, rsb, mode="row")
     check_f32(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows, exact accumulation")
+
+
+def test_full_dgrad():
+    d = workloads.dgrad()
+    say("dgrad 4096x7168x7168: quantise dY and W (dual) + GEMM on GPU")
+    qa, sa = fp8.fp8_quant_act_1x128(d["dy"].cuda())
+    _, _, qt, st = fp8.fp8_quant_weight_128x128_dual(d["w"].cuda())
+    y = fp8.fp8_block_gemm(qa, sa, qt, st)
+    torch.cuda.synchronize()
+    rows = _sample_rows(4096, 40, 3)
+    ra, rsa = quant.quant_1x128(f32(d["dy"][rows]))
+    rt, rst = quant.quant_128x128(np.ascontiguousarray(f32(d["w"]).T))
+    assert np.array_equal(qt.cpu().numpy(), rt)
+    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    ref = gemm.block_gemm(ra, rsa, rt, rst)
+    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows")
+    assert torch.isfinite(y.float()).all()

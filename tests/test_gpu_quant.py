@@ -138,6 +138,35 @@ def test_weight_small():
         assert_scales_equal(s, s_ref, what)
 
 
+def _weight_dual(w, what):
+    """Dual quantiser: row-major pair against the oracle on W, transposed pair
+    against the oracle on W^T (computed independently from the transposed input)."""
+    say(f"quant_weight dual {what} {tuple(w.shape)}")
+    N, K = w.shape
+    qb, q = guarded((N, K), torch.uint8)
+    sbuf, s = guarded((N // 128, K // 128), torch.float32)
+    qtb, qt = guarded((K, N), torch.uint8)
+    stbuf, st = guarded((K // 128, N // 128), torch.float32)
+    fp8.fp8_quant_weight_128x128_dual(w.cuda(), q, s, qt, st)
+    torch.cuda.synchronize()
+    for b in (qb, sbuf, qtb, stbuf):
+        check_guard(b)
+    wf = f32(w)
+    q_ref, s_ref = quant.quant_128x128(wf)
+    assert_codes_equal(q, q_ref, what)
+    assert_scales_equal(s, s_ref, what)
+    qt_ref, st_ref = quant.quant_128x128(np.ascontiguousarray(wf.T))
+    assert_codes_equal(qt, qt_ref, what + " transposed")
+    assert_scales_equal(st, st_ref, what + " transposed")
+
+
+def test_weight_dual_small():
+    _weight_dual(workloads.tiny()["w"], "tiny fp32")
+    _weight_dual(workloads.dense(M=1, N=384, K=1024)["w"], "dense-like bf16")
+    _weight_dual(workloads.dgrad(M=1, N=640, K=256)["w"], "dgrad-like bf16, N > K")
+    _weight_dual(torch.from_numpy(_special_tiles()[:8].reshape(8, 1024).repeat(16, axis=0)[:128]), "special")
+
+
 def test_validation_errors_reported():
     x = torch.zeros((4, 100), device="cuda")
     with pytest.raises(fp8.Fp8fgError) as e:
@@ -166,6 +195,10 @@ def test_full_quant_weight():
     q_ref, s_ref = quant.quant_128x128(f32(w))
     assert_codes_equal(q, q_ref, "weight full")
     assert_scales_equal(s, s_ref, "weight full")
+
+
+def test_full_dgrad_weight():
+    _weight_dual(workloads.dgrad()["w"], "dgrad W [7168,7168]")
 
 
 def test_full_wgrad_operands():

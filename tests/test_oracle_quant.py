@@ -160,6 +160,18 @@ def test_along_rows_is_the_transpose_case():
     assert np.array_equal(q, q2) and np.array_equal(s, s2)
 
 
+def test_weight_blocks_of_the_transpose():
+    """A 128x128 block of W^T is a block of W transposed, with the same amax, so
+    the block quantisation commutes with transposition (the data-gradient
+    operand): codes transpose, the scale grid transposes."""
+    x = workloads.dense(M=256, N=128, K=384)["x"].float().numpy()  # N(0,1) with x100 outliers
+    q, s = quant.quant_128x128(x)
+    assert np.any(q != q[:, ::-1])  # not trivially symmetric
+    qt, st = quant.quant_128x128(np.ascontiguousarray(x.T))
+    assert qt.shape == (384, 256) and st.shape == (3, 2)
+    assert np.array_equal(qt, q.T) and np.array_equal(st, s.T)
+
+
 def _near_midpoint_rows():
     """Rows whose elements sit within a few fp32 ulps of s * (E4M3 midpoint).
 
