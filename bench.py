@@ -297,12 +297,15 @@ def bench_quant(args, torch, fp8, workloads):
 
 
 def bench_moe(args, torch, fp8, workloads):
+    # One step of the MoE up-projection: quantise the 8192 tokens 1x128, then the
+    # grouped GEMM reads each routed row from its token (FP8 dispatch by index).
+    # The same GEMM on a pre-permuted copy of the rows is timed afterwards.
     route = workloads.moe_routing()
-    tokens = workloads.moe_tokens()
+    tokens = workloads.moe_tokens().cuda()
     offsets = torch.from_numpy(route["offsets"]).cuda()
-    xa = tokens.cuda()[torch.from_numpy(route["perm"]).cuda()]
+    idx = torch.from_numpy(route["perm"].astype("int32")).cuda()
     G, N, K = 256, 2048, 7168
-    Mt = xa.shape[0]
+    T, Mt = tokens.shape[0], idx.numel()
     # Weights drawn on the GPU from a seeded generator: the benchmark needs no
     # oracle comparison, and 3.76e9 CPU draws would dominate the run time.
     gen = torch.Generator(device="cuda").manual_seed(4)
@@ -310,38 +313,57 @@ def bench_moe(args, torch, fp8, workloads):
     qb, sb = fp8.fp8_quant_weight_128x128(w)
     del w
     qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
-    qa = torch.empty((Mt, K), dtype=torch.uint8, device="cuda")
-    sa = torch.empty((Mt, K // 128), dtype=torch.float32, device="cuda")
+    qt = torch.empty((T, K), dtype=torch.uint8, device="cuda")
+    st = torch.empty((T, K // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
-    tq, tg = Timer(torch, args.steps), Timer(torch, args.steps)
+    tg = Timer(torch, args.steps)
+    tq, tp = Timer(torch, 1), Timer(torch, args.steps)
+
+    def step(timed):
+        fp8.fp8_quant_act_1x128(tokens, qt, st)
+        if timed:
+            with tg:
+                fp8.fp8_block_grouped_gemm_gather(qt, st, idx, offsets, qb, sb, accum="fp8", y=y)
+        else:
+            fp8.fp8_block_grouped_gemm_gather(qt, st, idx, offsets, qb, sb, accum="fp8", y=y)
+
     for _ in range(args.warmup):
-        fp8.fp8_quant_act_1x128(xa, qa, sa)
-        fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
+        step(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        with tq:
-            fp8.fp8_quant_act_1x128(xa, qa, sa)
-        with tg:
-            fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
+        step(True)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    with tq:
+        for _ in range(args.steps):
+            fp8.fp8_quant_act_1x128(tokens, qt, st)
+    # the same GEMM on routed rows copied out in advance (no gather)
+    qa, sa = qt[idx.long()].contiguous(), st[idx.long()].contiguous()
+    for _ in range(args.steps):
+        with tp:
+            fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
+    torch.cuda.synchronize()
     flop = 2.0 * Mt * N * K
-    gms = tg.mean_ms()
-    gemm_bytes = Mt * K + Mt * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4 + Mt * N * 2
+    gms, pms = tg.mean_ms(), tp.mean_ms()
+    gemm_bytes = T * K + T * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4 + Mt * N * 2 + Mt * 4
+
+    def gemm_line(ms):
+        return {"ms": ms, "TFLOP/s": flop / (ms * 1e-3) / 1e12, "frac_fp8_peak": flop / (ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                "GB/s": gemm_bytes / (ms * 1e-3) / 1e9, "frac_hbm": gemm_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
     return {
         "metric": "grouped FP8 GEMM TFLOP/s", "value": flop / dt / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
-        "config": {"workload": "MoE up-projection: 8192 tokens x 7168, 256 experts top-8 -> 65536 rows; "
-                               "per-expert W [2048,7168]; 1x128 quant of the dispatched rows + grouped GEMM, bf16 out",
-                   "M_total": Mt, "N": N, "K": K, "G": G},
+        "config": {"workload": "MoE up-projection: 8192 tokens x 7168, 256 experts top-8 -> 65536 routed rows; "
+                               "per-expert W [2048,7168]; 1x128 quantisation of the tokens, grouped GEMM reading "
+                               "each routed row from its token by index, bf16 out",
+                   "T": T, "M_total": Mt, "N": N, "K": K, "G": G},
         "kernels": {
-            "fp8_quant_act_1x128": _hbm_line("act", tq.mean_ms(), Mt * K * 3 + Mt * (K // 128) * 4, {}),
-            "fp8_block_grouped_gemm": {"ms": gms, "TFLOP/s": flop / (gms * 1e-3) / 1e12,
-                                       "frac_fp8_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                                       "GB/s": gemm_bytes / (gms * 1e-3) / 1e9,
-                                       "frac_hbm": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "fp8_quant_act_1x128 (tokens)": _hbm_line("act", tq.mean_ms() / args.steps, T * K * 3 + T * (K // 128) * 4, {}),
+            "fp8_block_grouped_gemm_gather": gemm_line(gms),
+            "fp8_block_grouped_gemm (pre-permuted rows)": gemm_line(pms),
         },
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -37,6 +37,9 @@ _SIGS = {
     "fp8_block_grouped_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64,
                                _c.c_int64, _c.c_int64, _c.c_void_p],
+    "fp8_block_grouped_gemm_gather": [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p,
+                                      _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
+                                      _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8fg_status_string": [_c.c_int],
     "fp8fg_abi_version": [],
 }
@@ -206,4 +209,27 @@ def fp8_block_grouped_gemm(a, sa, offsets, b, sb, accum=None, out_dtype=torch.bf
                                       _accum_code(accum, y.dtype), _ptr(y), _dtype_code(y.dtype),
                                       M, N, K, _stream(stream))
     _check("fp8_block_grouped_gemm", st)
+    return y
+
+
+def fp8_block_grouped_gemm_gather(a_tok, sa_tok, row_index, offsets, b, sb, accum=None,
+                                  out_dtype=torch.bfloat16, y=None, stream=None):
+    """Grouped GEMM whose row r is token ``row_index[r]`` of ``a_tok`` [T, K]
+    (``row_index`` device int32 [M_total]); Y stays in routed-row order."""
+    _on_gpu(a_tok, sa_tok, row_index, offsets, b, sb)
+    T, K = a_tok.shape
+    G, N, _ = b.shape
+    M = row_index.numel()
+    if offsets.dtype != torch.int32 or offsets.numel() != G + 1:
+        raise ValueError("offsets must be int32 [G+1]")
+    if row_index.dtype != torch.int32:
+        raise ValueError("row_index must be int32")
+    if y is None:
+        y = torch.empty((M, N), dtype=out_dtype, device=a_tok.device)
+    _on_gpu(y)
+    _contig(a_tok, sa_tok, row_index, offsets, b, sb, y)
+    st = lib().fp8_block_grouped_gemm_gather(_ptr(a_tok), _ptr(sa_tok), T, _ptr(row_index), _ptr(offsets), G,
+                                             _ptr(b), _ptr(sb), _accum_code(accum, y.dtype), _ptr(y),
+                                             _dtype_code(y.dtype), M, N, K, _stream(stream))
+    _check("fp8_block_grouped_gemm_gather", st)
     return y

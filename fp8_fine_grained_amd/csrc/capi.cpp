@@ -140,4 +140,22 @@ int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* gro
   return hip_status(fp8fg::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_block_grouped_gemm_gather(const uint8_t* a_tok, const float* sa_tok, int64_t T, const int32_t* row_index,
+                                  const int32_t* group_offsets, int64_t G, const uint8_t* b, const float* sb,
+                                  int accum, void* y, int y_dtype, int64_t M_total, int64_t N, int64_t K,
+                                  fp8fg_stream_t stream) {
+  if (G < 0 || T < 0) return FP8FG_ERR_INVALID_ARG;
+  const int c = check_gemm_common(a_tok, sa_tok, b, sb, accum, y, y_dtype, M_total, N, K);
+  if (c < 0 || G == 0) return c > 0 ? c : FP8FG_OK;
+  if (c != FP8FG_OK) return c;
+  if (T == 0 || !group_offsets || !row_index) return FP8FG_ERR_INVALID_ARG;
+  if (!aligned(group_offsets, 4) || !aligned(row_index, 4)) return FP8FG_ERR_MISALIGNED;
+  if (G > kInt32Max || (M_total / 128 + G) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (T > kInt32Max || T * K >= (int64_t(1) << 32)) return FP8FG_ERR_UNSUPPORTED;  // 32-bit row offsets
+  fp8fg::GemmArgs g{a_tok, sa_tok, b, sb, y, group_offsets, M_total, N, K, G,
+                    false, accum == FP8FG_ACCUM_EXACT, y_dtype == FP8FG_BF16, row_index, T};
+  if (!fp8fg::fp8_block_kernel_applies(g)) return FP8FG_ERR_UNSUPPORTED;  // N % 256 != 0
+  return hip_status(fp8fg::launch_grouped_gemm_gather(g, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

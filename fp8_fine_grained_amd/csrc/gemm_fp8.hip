@@ -64,7 +64,8 @@ struct FParams {
   const float* sb;
   void* y;
   const int32_t* offsets;
-  int64_t M, N, K, G;
+  const int32_t* rows;  // gather: row r of the grouped problem is row rows[r] of a / sa
+  int64_t M, N, K, G, T;
   int KB;  // K / 128
   int MT;  // m-tiles (dense: ceil(M/BM); grouped: upper bound M/BM + G)
   int NT;  // N / BN
@@ -169,7 +170,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // EXACT: operands widened to fp16 and multiplied by fp16 MFMAs (every product and
 // every in-instruction sum exact); ROWS: one weight-side scale per row n and
 // K block instead of one per 128 x 128 block.
-template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED>
+// GATHER (grouped only): A rows and their scales are read through p.rows.
+template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED,
+          bool GATHER = false>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) {
   static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
   constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
@@ -188,6 +191,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   constexpr int WAIT_N = (STAGES - 2) * LOADS;
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(!(ROWS && GROUPED), "grouped weights carry block scales");
+  static_assert(!GATHER || GROUPED, "gathering is a grouped-GEMM mode");
   // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
   // padded by 16) in its own slice of the tile buffer.
   constexpr int EPI_PITCH = TN * 2 + 16;
@@ -297,8 +301,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // slot, so every wavefront issues exactly LOADS loads per stage.
   const int lrow = lane >> 3;
   const int lchunk = ((lane & 7) ^ lrow) * 16;
-  // Byte offsets within the tile's row panels (below 256 * K < 2^32).
-  const uint8_t* a_base = uniform_ptr(p.a + row_lo * p.K);
+  // Source row of A (and of its scales) for tile row `row` (in [row_lo, row_hi)).
+  auto a_row = [&](int64_t row) -> int64_t {
+    if constexpr (GATHER) {
+      int64_t t = p.rows[row];
+      return t < 0 ? 0 : (t >= p.T ? p.T - 1 : t);
+    } else {
+      return row;
+    }
+  };
+  // Byte offsets within the tile's row panels (below 256 * K < 2^32), or from
+  // the start of A when gathering (below T * K < 2^32).
+  const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + row_lo * p.K);
   const uint8_t* b_base = uniform_ptr(bmat + n0 * p.K);
   uint32_t va[A_DMA], vb[B_DMA];
   uint64_t a_live[A_DMA];  // grouped: lanes whose tile row lies inside the segment
@@ -308,7 +322,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     int64_t row = row_lo + r;
     a_live[i] = __ballot(row < row_hi);
     row = row < row_hi ? row : row_hi - 1;
-    va[i] = static_cast<uint32_t>((row - row_lo) * p.K + lchunk);
+    va[i] = static_cast<uint32_t>((GATHER ? a_row(row) : row - row_lo) * p.K + lchunk);
   }
 #pragma unroll
   for (int i = 0; i < B_DMA; ++i) vb[i] = static_cast<uint32_t>((wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk);
@@ -316,7 +330,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   if (wave < SA_WAVES) {
     int64_t row = row_lo + wave * 64 + lane;
     row = row < row_hi ? row : row_hi - 1;
-    gs = p.sa + row * p.KB;
+    gs = p.sa + a_row(row) * p.KB;
   } else if constexpr (ROWS) {
     int w = wave - SA_WAVES;
     w = w < SB_WAVES ? w : 0;  // filler wavefronts re-read the first weight rows' scales
@@ -559,21 +573,23 @@ template <int CFG> struct Cfg;
 template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
 
-template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED>
+template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER = false>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using C = Cfg<CFG>;
   const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
-  FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.M, g.N, g.K, g.G,
+  FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.row_index, g.M, g.N, g.K, g.G, g.T,
             static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN)};
   const unsigned blocks = static_cast<unsigned>(MT * p.NT);
-  hipLaunchKernelGGL((gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED>),
-                     dim3(blocks), dim3(NTHREADS), 0, s, p);
+  hipLaunchKernelGGL(
+      (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER>),
+      dim3(blocks), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
-template <int CFG, bool EXACT, bool ROWS, bool GROUPED>
+template <int CFG, bool EXACT, bool ROWS, bool GROUPED, bool GATHER = false>
 hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
-  return g.y_bf16 ? launch_cfg<CFG, EXACT, ROWS, true, GROUPED>(g, s) : launch_cfg<CFG, EXACT, ROWS, false, GROUPED>(g, s);
+  return g.y_bf16 ? launch_cfg<CFG, EXACT, ROWS, true, GROUPED, GATHER>(g, s)
+                  : launch_cfg<CFG, EXACT, ROWS, false, GROUPED, GATHER>(g, s);
 }
 
 }  // namespace
@@ -588,6 +604,10 @@ bool fp8_block_kernel_applies(const GemmArgs& g) {
 // ~256 rows then waste less of their last m-tile).  The exact mode (fp16
 // operands, twice the fragment registers) and the row-scaled mode (one more
 // multiply and four row scales per sub-tile) use the 64 x 64 wavefront tile.
+hipError_t launch_grouped_gemm_gather(const GemmArgs& g, hipStream_t s) {
+  return g.exact ? launch_out<1, true, false, true, true>(g, s) : launch_out<1, false, false, true, true>(g, s);
+}
+
 hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s) {
   if (grouped)
     return g.exact ? launch_out<1, true, false, true>(g, s) : launch_out<1, false, false, true>(g, s);

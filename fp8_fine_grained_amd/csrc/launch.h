@@ -31,9 +31,13 @@ struct GemmArgs {
   bool row_scales;  // B scales per row (1x128) instead of per 128x128 block
   bool exact;       // exact products (fp16 matrix cores) instead of FP8 MFMA
   bool y_bf16;
+  const int32_t* row_index = nullptr;  // grouped with gather: row r of A is a[row_index[r]]
+  int64_t T = 0;                       // rows of a (and sa) when gathering
 };
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
+// Grouped GEMM gathering A rows by index (requires fp8_block_kernel_applies).
+hipError_t launch_grouped_gemm_gather(const GemmArgs& g, hipStream_t s);
 
 // 256x256-tile FP8-accumulation kernel for 128x128 weight scales (gemm_fp8.hip).
 bool fp8_block_kernel_applies(const GemmArgs& g);

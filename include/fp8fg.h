@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 2
+#define FP8FG_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum {
@@ -188,6 +188,28 @@ int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* gro
                            int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
                            int y_dtype, int64_t M_total, int64_t N, int64_t K,
                            fp8fg_stream_t stream);
+
+/*
+ * The grouped GEMM reading its rows through an index: FP8 dispatch without a
+ * permuted copy of the activations (the innerforce notes dispatch activations
+ * in FP8; here the dispatch is the index).  Tokens are quantised once, 1x128,
+ * and each routed row is read from its token row where the GEMM needs it.
+ *
+ * Row r of the grouped problem is token row_index[r]:
+ *     Y[r,:] = deq(a_tok[row_index[r], :]) * deq(B[g])^T,  r in segment g.
+ * a_tok      uint8 E4M3 [T, K] row-major;  sa_tok fp32 [T, K/128]
+ * row_index  DEVICE int32 [M_total], values in [0, T) (values outside are
+ *            clamped into it: unspecified rows, never an access outside a_tok)
+ * group_offsets, G, b, sb, accum, y, y_dtype, M_total, N, K
+ *            as fp8_block_grouped_gemm (y stays in routed-row order).
+ * Requires N % 256 == 0, K % 128 == 0, T * K < 2^32 (32-bit row offsets),
+ * T >= 1 when M_total > 0; row_index 4-byte aligned; other alignment as
+ * fp8_block_gemm.  M_total == 0 or G == 0 is a no-op.
+ */
+int fp8_block_grouped_gemm_gather(const uint8_t* a_tok, const float* sa_tok, int64_t T,
+                                  const int32_t* row_index, const int32_t* group_offsets, int64_t G,
+                                  const uint8_t* b, const float* sb, int accum, void* y, int y_dtype,
+                                  int64_t M_total, int64_t N, int64_t K, fp8fg_stream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fp8fg_status_string(int status);

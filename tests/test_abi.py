@@ -21,14 +21,14 @@ def L():
 def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_quant_weight_128x128_dual",
-                          "fp8_block_gemm", "fp8_block_grouped_gemm", "fp8fg_status_string",
-                          "fp8fg_abi_version"}
+                          "fp8_block_gemm", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
+                          "fp8fg_status_string", "fp8fg_abi_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 2
+    assert L.fp8fg_abi_version() == 3
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -106,3 +106,20 @@ def test_grouped_validation(L):
     assert f(*args(N=192)) == fp8.ERR_UNSUPPORTED
     assert f(*args(G=0)) == fp8.OK
     assert f(*args(M=0, a=NULL)) == fp8.OK
+
+
+def test_grouped_gather_validation(L):
+    f = L.fp8_block_grouped_gemm_gather
+    ok = dict(a=GOOD, sa=GOOD, T=32, idx=GOOD, off=GOOD, G=4, b=GOOD, sb=GOOD, accum=fp8.ACCUM_FP8_MFMA,
+              y=GOOD, ydt=fp8.BF16, M=64, N=256, K=256, s=NULL)
+    args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
+    assert f(*args(G=-1)) == fp8.ERR_INVALID_ARG
+    assert f(*args(T=-1)) == fp8.ERR_INVALID_ARG
+    assert f(*args(T=0)) == fp8.ERR_INVALID_ARG
+    assert f(*args(idx=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(off=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(idx=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(N=128)) == fp8.ERR_UNSUPPORTED  # gathering needs N % 256 == 0
+    assert f(*args(T=1 << 20, K=1 << 13)) == fp8.ERR_UNSUPPORTED  # T * K >= 2^32
+    assert f(*args(G=0)) == fp8.OK
+    assert f(*args(M=0, a=NULL, idx=NULL)) == fp8.OK

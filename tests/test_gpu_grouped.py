@@ -66,6 +66,66 @@ def test_single_group_matches_dense_kernel():
     assert torch.equal(yg, yd)
 
 
+def _gather_case(T, G, topk, N, K, seed):
+    """Tokens routed top-k over G experts; the gathered GEMM reads token rows
+    through the permutation, the reference reads an explicitly permuted copy."""
+    logits = workloads.dense(seed=seed, M=T, N=1, K=G)["x"].float().numpy()
+    route = workloads.route_topk(logits, np.zeros(G, np.float32), topk)
+    perm, offsets = route[0], route[1]
+    x = workloads.dense(seed=seed + 1, M=T, N=128, K=K)["x"]
+    w = torch.stack([workloads.moe_expert_weight(g, seed=seed, N=N, K=K) for g in range(G)])
+    qt, st = fp8.fp8_quant_act_1x128(x.cuda())
+    qb, sb = fp8.fp8_quant_weight_128x128(w.cuda().view(G * N, K))
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    idx = torch.from_numpy(perm.astype(np.int32)).cuda()
+    off = torch.from_numpy(offsets).cuda()
+    rt, rst = quant.quant_1x128(f32(x))
+    assert np.array_equal(qt.cpu().numpy(), rt)
+    rb = np.empty((G, N, K), np.uint8)
+    rsb = np.empty((G, N // 128, K // 128), np.float32)
+    for g in range(G):
+        rb[g], rsb[g] = quant.quant_128x128(f32(w[g]))
+    ref = gemm.grouped_gemm(rt[perm], rst[perm], offsets, rb, rsb)
+    return (qt, st, idx, off, qb, sb), ref, int(offsets[-1])
+
+
+def test_gather_small():
+    g, ref, M = _gather_case(T=97, G=8, topk=3, N=256, K=384, seed=21)
+    qt, st, idx, off, qb, sb = g
+    say(f"grouped gather: 97 tokens, 8 experts top-3 -> {M} rows, N=256, K=384")
+    for accum, dtype in (("fp8", torch.bfloat16), ("exact", torch.float32), ("fp8", torch.float32)):
+        buf, y = guarded((M, 256), dtype)
+        fp8.fp8_block_grouped_gemm_gather(qt, st, idx, off, qb, sb, accum=accum, y=y)
+        torch.cuda.synchronize()
+        check_guard(buf)
+        if dtype == torch.bfloat16:
+            check_bf16(y, ref, "fp8 accum, bf16")
+        elif accum == "exact":
+            check_f32(y, ref, "exact accum fp32")
+        # Gathering only moves the loads: bitwise the same as the grouped GEMM on a permuted copy.
+        yp = fp8.fp8_block_grouped_gemm(qt[idx.long()].contiguous(), st[idx.long()].contiguous(), off, qb, sb,
+                                        accum=accum, out_dtype=dtype)
+        assert torch.equal(y, yp), f"{accum} {dtype}"
+
+
+def test_gather_repeated_and_unused_tokens():
+    # every routed row is token 5 or token 0; most tokens are never read
+    T, K, N, G = 40, 256, 256, 3
+    x = workloads.dense(seed=31, M=T, N=128, K=K)["x"]
+    qt, st = fp8.fp8_quant_act_1x128(x.cuda())
+    w = torch.stack([workloads.moe_expert_weight(g, seed=31, N=N, K=K) for g in range(G)])
+    qb, sb = fp8.fp8_quant_weight_128x128(w.cuda().view(G * N, K))
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    perm = np.array([5, 0, 5, 5, 0, 5, 0], np.int32)
+    offsets = np.array([0, 2, 2, 7], np.int32)
+    y = fp8.fp8_block_grouped_gemm_gather(qt, st, torch.from_numpy(perm).cuda(), torch.from_numpy(offsets).cuda(),
+                                          qb, sb, accum="exact", out_dtype=torch.float32)
+    rt, rst = quant.quant_1x128(f32(x))
+    rb = np.stack([quant.quant_128x128(f32(w[g]))[0] for g in range(G)])
+    rsb = np.stack([quant.quant_128x128(f32(w[g]))[1] for g in range(G)])
+    check_f32(y, gemm.grouped_gemm(rt[perm], rst[perm], offsets, rb, rsb), "repeated tokens, exact")
+
+
 def test_empty_inputs_are_noops():
     K, N = 256, 128
     a = torch.empty((0, K), dtype=torch.uint8, device="cuda")
@@ -113,3 +173,9 @@ def test_full_moe_up_projection():
         sel = np.nonzero(expert_of == e)[0]
         ref[sel] = gemm.block_gemm(ra[sel], rsa[sel], qe, se)
     check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows")
+    say("  FP8 dispatch by index: quantise the 8192 tokens, gather rows inside the GEMM")
+    qt, st = fp8.fp8_quant_act_1x128(tokens.cuda())
+    idx = perm.to(torch.int32).cuda()
+    assert torch.equal(qt[idx.long()], qa) and torch.equal(st[idx.long()], sa)
+    yg = fp8.fp8_block_grouped_gemm_gather(qt, st, idx, torch.from_numpy(offsets).cuda(), qb, sb)
+    assert torch.equal(yg, y)
