@@ -500,8 +500,10 @@ def copy_calibration(args, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # The first ~100 dense GEMMs of a process run up to 25% slower while the
+    # clocks ramp up; the default warm-up covers that ramp.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")

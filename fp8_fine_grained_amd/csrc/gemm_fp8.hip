@@ -29,6 +29,11 @@
 //    lane of a fragment read takes logical chunks j and j+4 (j = lane / 16) of
 //    row lane % 16: measured bank-conflict free for ds_read_b128 on gfx950.
 //  * The per-block scales are staged the same way (global_load_lds_dword).
+//  * Dense 256 x 256 tiles also touch K block kb+3 while multiplying block kb
+//    (one dword per 128-byte line, each line once per XCD), so operands that
+//    only HBM holds (just written by the quantisers) reach L2 before the DMAs
+//    of block kb+2 ask for them; without it the GEMM runs ~12% slower right
+//    after the quantisers than back to back.
 //  * v_mfma_f32_16x16x128_f8f6f4 forms each sub-tile's 128-K partial; the
 //    promotion acc += P * sa[m,kb] * sb[nb,kb] is one VALU FMA per output, the
 //    factor being one value per lane and sub-tile column because the MFMA
@@ -312,20 +317,23 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   };
   // Byte offsets within the tile's row panels (below 256 * K < 2^32), or from
   // the start of A when gathering (below T * K < 2^32).
-  const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + row_lo * p.K);
-  const uint8_t* b_base = uniform_ptr(bmat + n0 * p.K);
-  uint32_t va[A_DMA], vb[B_DMA];
-  uint64_t a_live[A_DMA];  // grouped: lanes whose tile row lies inside the segment
+  // Contiguous operands: every DMA of a wavefront uses the same lane offset
+  // (row lrow, chunk lchunk); the wavefront's row block and the DMA's 8-row step
+  // are folded into the wave-uniform base.  Gathered rows keep one offset per DMA.
+  const int uw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + (row_lo + uw * (BM / 8)) * p.K);
+  const uint8_t* b_base = uniform_ptr(bmat + (n0 + uw * (BN / 8)) * p.K);
+  const uint32_t voff = static_cast<uint32_t>(lrow * p.K + lchunk);
+  uint32_t va[GATHER ? A_DMA : 1];
+  uint64_t a_live[A_DMA];  // lanes whose tile row lies inside the segment (or the matrix)
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
     const int r = wave * (BM / 8) + i * 8 + lrow;
     int64_t row = row_lo + r;
     a_live[i] = __ballot(row < row_hi);
     row = row < row_hi ? row : row_hi - 1;
-    va[i] = static_cast<uint32_t>((GATHER ? a_row(row) : row - row_lo) * p.K + lchunk);
+    if constexpr (GATHER) va[i] = static_cast<uint32_t>(a_row(row) * p.K + lchunk);
   }
-#pragma unroll
-  for (int i = 0; i < B_DMA; ++i) vb[i] = static_cast<uint32_t>((wave * (BN / 8) + i * 8 + lrow) * p.K + lchunk);
   const float* gs;
   if (wave < SA_WAVES) {
     int64_t row = row_lo + wave * 64 + lane;
@@ -348,19 +356,45 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
                           : (b_scale_wave ? lds_addr(&s_sb[0][(uwave - SA_WAVES) * 64]) : lds_addr(s_filler));
   const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (b_scale_wave ? SB_LEN * 4 : 0);
 
+  // L2 prefetch (256 x 256 dense tiles): in iteration kb every wavefront touches
+  // one dword of K block kb + PF_DIST in 12 rows, so the lines are on their way
+  // from HBM two iterations before the DMAs ask for them (the DMAs' own lead is
+  // one iteration, which covers the latency of the last-level cache but not that
+  // of HBM, e.g. right after the quantisers have written the operands).  The
+  // tiles that run at the same time on one XCD share their panels (with the
+  // band order: 8 n-tiles per A panel, 4 m-tiles per B panel), so each tile
+  // touches one slice, 32 A rows and 64 B rows, and each line is requested
+  // about once per XCD.  The loads land in the scratch slot, never read.
+  constexpr int PF_DIST = 3;
+  constexpr int PF = (GROUPED || BM + BN != NTHREADS) ? 0 : PF_DIST;
+  const uint8_t* pf_ptr = nullptr;
+  if constexpr (PF > 0) {
+    const int live = static_cast<int>(row_hi - row_lo);
+    const int slot = uw * 12 + lane % 12;  // 96 rows over 8 wavefronts
+    if (slot < BM / 8) {
+      int r = (nt % 8) * (BM / 8) + slot;
+      r = r < live ? r : live - 1;
+      pf_ptr = p.a + (row_lo + r) * p.K;
+    } else {
+      pf_ptr = bmat + (n0 + (mt % 4) * (BN / 4) + (slot - BM / 8)) * p.K;
+    }
+  }
+  auto prefetch = [&](int kb) {
+    if constexpr (PF > 0) dma4(pf_ptr + static_cast<int64_t>(kb) * 128, lds_addr(s_filler));
+  };
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
   constexpr int SPREAD = SN >= 8 ? 6 : (SN >= 4 ? SN / 2 : SN);  // sub-tile steps that issue them
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
     if (d < A_DMA) {
-      if constexpr (GROUPED)
+      if constexpr (GATHER)
         dma16_masked(a_base + kof, va[d], lds_ta + so + d * 1024, a_live[d]);
       else
-        dma16(a_base + kof, va[d], lds_ta + so + d * 1024);
+        dma16_masked(a_base + kof + static_cast<int64_t>(d) * 8 * p.K, voff, lds_ta + so + d * 1024, a_live[d]);
+    } else {
+      dma16(b_base + kof + static_cast<int64_t>(d - A_DMA) * 8 * p.K, voff, lds_tb + so + (d - A_DMA) * 1024);
     }
-    else
-      dma16(b_base + kof, vb[d - A_DMA], lds_tb + so + (d - A_DMA) * 1024);
   };
   auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
   auto issue = [&](int kb, int st) {
@@ -377,8 +411,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 
   const int KB = p.KB;
   auto clampkb = [&](int kb) { return kb < KB ? kb : KB - 1; };
-  if constexpr (GROUPED) {
-    // Rows past the end of the expert's segment are never loaded: their LDS
+  {
+    // Rows past the end of the expert's segment (or of the matrix) are never loaded: their LDS
     // slots are zeroed once here, so their MFMAs multiply zeros (which costs the
     // matrix cores far less power than the clamped copies of a real row would)
     // and their outputs, never stored, are zero.
@@ -395,7 +429,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // prologue: blocks 0 .. STAGES-2 into stages 0 .. STAGES-2
 #pragma unroll
   for (int s0 = 0; s0 < STAGES - 1; ++s0) issue(clampkb(s0), s0);
-  wait_barrier<WAIT_N>();  // block 0 resident
+  constexpr int PF_PRO = PF > STAGES ? PF - STAGES : 0;  // blocks STAGES .. PF-1, before the loop's
+#pragma unroll
+  for (int q = 0; q < PF_PRO; ++q) prefetch(clampkb(STAGES + q));
+  // (loads complete in order: waiting for all but the newest PF_PRO retires block 0's DMAs)
+  wait_barrier<WAIT_N + PF_PRO>();  // block 0 resident
 
   // Fragments of the current block: all m sub-tiles, the first n sub-tile, and
   // the per-column promotion factors sa[m,kb] * sb[nb,kb] (block mode) or sa[m,kb]
@@ -484,6 +522,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
         // keep the per-wavefront load count uniform are only needed with more.
         if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
       }
+      if (i == SN - 2) prefetch(clampkb(kb + PF));  // after this iteration's DMAs
       const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
       if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
       WideFrag wn_frag;
@@ -500,7 +539,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     // run after the barrier, and the next block's fragments are requested as
     // each m fragment is consumed, so their LDS latency hides under the MFMAs.
     __builtin_amdgcn_s_setprio(0);
-    wait_barrier<WAIT_N>();
+    // the newest load, this iteration's prefetch, may stay in flight
+    wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
     st = st == STAGES - 1 ? 0 : st + 1;
     float f_old[SM];
 #pragma unroll
