@@ -216,8 +216,38 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // ---- tile selection
   const int T = p.MT * p.NT;
   const int bid = blockIdx.x;
-  const int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
   int mt, nt;
+  if constexpr (GROUPED) {
+    // The grid covers an upper bound of the m-tiles; the live ones are counted
+    // here (from the device offsets) and dealt out in equal XCD bands, so that
+    // the workgroups left over, which exit at once, are spread over all XCDs
+    // instead of filling the last bands.
+    if (wave == 0) {
+      int total = 0;
+      for (int64_t base = 0; base < p.G; base += 64) {
+        const int64_t g = base + lane;
+        int cnt = 0;
+        if (g < p.G) {
+          int64_t lo = p.offsets[g], hi = p.offsets[g + 1];
+          lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
+          hi = hi < lo ? lo : (hi > p.M ? p.M : hi);
+          cnt = static_cast<int>((hi - lo + BM - 1) / BM);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
+        total += cnt;
+      }
+      if (lane == 0) tile_info[0] = total;
+    }
+    __syncthreads();
+    const int live = tile_info[0] * p.NT;  // <= T
+    if (T % 8 == 0) {
+      const int band = (live + 7) / 8;
+      t = bid / 8 < band ? (bid % 8) * band + bid / 8 : T;  // T: no tile
+    }
+    __syncthreads();  // tile_info is rewritten below
+  }
   if constexpr (!GROUPED) {
     const int band = t / (GROUP_M * p.NT);
     const int first = band * GROUP_M;
