@@ -33,6 +33,23 @@ dequantised value dec(q) * s is exactly zero.  Non-finite inputs and groups
 whose scale would be subnormal (0 < amax < 448 * 2^-126) are outside the
 contract and raise ValueError.
 
+Power-of-two scales (the ``*_pow2`` functions).  The innerforce notes'
+Figure 7(a) passage calls the grouping consistent with microscaling formats,
+and the tonho.wtf entry's "o que isso custou" wish list asks for an MMA that
+applies per-group scales itself.  Microscaling scales are powers of two (the
+E8M0 format), which is what gfx950's scaled matrix-core instructions take.
+The pages fix neither that format nor its rounding; the reading taken keeps
+the pages' scaling rule (the group's amax lands on or below 448, nothing is
+clipped) with the scale restricted to powers of two:
+
+    s    = 2^e, e the smallest integer with amax <= 448 * 2^e
+           (so 224 < amax / s <= 448)
+    inv  = 2^-e                              (exact)
+    y_i  = fl32(x_i * inv),  q_i = E4M3 RNE cast of y_i (as above)
+
+An all-zero group again gets s = 0 and inv = 0.  Groups whose e or -e falls
+outside fp32's normal exponent range are outside the contract.
+
 Parity: pinned.  tests/test_oracle_quant.py checks hand-worked tiles
 (tests/golden/quant_tiles_handworked.json), the amax -> 0x7E invariant, the
 quantise-dequantise error bound, power-of-two and sign equivariance, the
@@ -59,6 +76,25 @@ def _scale_and_inverse(amax):
     return s.astype(np.float32), inv.astype(np.float32)
 
 
+def _pow2_scale_and_inverse(amax):
+    """Power-of-two scale 2^e (smallest e with amax <= 448 * 2^e) and 2^-e."""
+    a = np.asarray(amax, dtype=np.float32).astype(np.float64)
+    nz = a != 0
+    # a = f * 2^E with f in [0.5, 1): a * 2^-(E-9) = f * 2^9 lies in [256, 512);
+    # it is within 448 unless f > 7/8, and one power of two more always is.
+    _, E = np.frexp(a)
+    e = E - 9
+    e = np.where(np.ldexp(a, -e) > E4M3_MAX, e + 1, e)
+    if np.any(nz & ((e < -126) | (e > 126))):
+        raise ValueError("quant: power-of-two scale outside fp32's normal range is outside the contract")
+    s = np.where(nz, np.ldexp(1.0, e), 0.0).astype(np.float32)
+    inv = np.where(nz, np.ldexp(1.0, -e), 0.0).astype(np.float32)
+    return s, inv
+
+
+_SCALES = {"amax": _scale_and_inverse, "pow2": _pow2_scale_and_inverse}
+
+
 def _check_input(x):
     x = np.asarray(x)
     if x.ndim != 2:
@@ -69,14 +105,15 @@ def _check_input(x):
     return x
 
 
-def quant_1x128(x):
+def quant_1x128(x, scale="amax"):
     """Quantise ``x`` [M, K] in 1x128 tiles along K.
 
     Returns ``(q, s)``: uint8 E4M3 codes [M, K] and fp32 scales
     [M, ceil(K/128)], where ``s[m, g]`` belongs to columns
     ``128*g .. 128*g+127`` of row ``m`` (a ragged last group covers the
-    columns present).
+    columns present).  ``scale="pow2"`` takes power-of-two scales.
     """
+    scale_and_inverse = _SCALES[scale]
     x = _check_input(x)
     M, K = x.shape
     G = -(-K // GROUP)
@@ -86,19 +123,21 @@ def quant_1x128(x):
         cols = slice(g * GROUP, min(K, (g + 1) * GROUP))
         tile = x[:, cols]
         amax = np.max(np.abs(tile), axis=1) if tile.size else np.zeros(M, np.float32)
-        sg, inv = _scale_and_inverse(amax)
+        sg, inv = scale_and_inverse(amax)
         s[:, g] = sg
         q[:, cols] = encode(tile * inv[:, None])
     return q, s
 
 
-def quant_128x128(w):
+def quant_128x128(w, scale="amax"):
     """Quantise ``w`` [N, K] in 128x128 blocks.
 
     Returns ``(q, s)``: uint8 codes [N, K] and fp32 scales
     [ceil(N/128), ceil(K/128)], where ``s[i, j]`` belongs to rows
-    ``128*i ..`` and columns ``128*j ..`` of ``w``.
+    ``128*i ..`` and columns ``128*j ..`` of ``w``.  ``scale="pow2"`` takes
+    power-of-two scales.
     """
+    scale_and_inverse = _SCALES[scale]
     w = _check_input(w)
     N, K = w.shape
     GN, GK = -(-N // GROUP), -(-K // GROUP)
@@ -109,7 +148,7 @@ def quant_128x128(w):
         for j in range(GK):
             cols = slice(j * GROUP, min(K, (j + 1) * GROUP))
             block = w[rows, cols]
-            sb, inv = _scale_and_inverse(np.max(np.abs(block)))
+            sb, inv = scale_and_inverse(np.max(np.abs(block)))
             s[i, j] = sb
             q[rows, cols] = encode(block * inv)
     return q, s

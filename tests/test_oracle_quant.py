@@ -28,10 +28,11 @@ def test_handworked_tiles(case):
         x[tuple(idx) if isinstance(idx, list) else (0, idx)] = np.float32(v)
     for idx, c in case["expected_codes"]:
         codes[tuple(idx) if isinstance(idx, list) else (0, idx)] = int(c, 16)
-    if case["kind"] == "act_1x128":
-        q, s = quant.quant_1x128(x)
+    scale = "pow2" if case["kind"].endswith("_pow2") else "amax"
+    if case["kind"].startswith("act_1x128"):
+        q, s = quant.quant_1x128(x, scale=scale)
     else:
-        q, s = quant.quant_128x128(x)
+        q, s = quant.quant_128x128(x, scale=scale)
     want_s = [int(b, 16) for b in case["expected_scale_bits"]]
     assert s.reshape(-1).view(np.uint32).tolist() == want_s
     bad = np.argwhere(q != codes)
@@ -238,3 +239,75 @@ def test_out_of_contract_inputs_raise():
     x[0, 0] = np.inf
     with pytest.raises(ValueError):
         quant.quant_1x128(x)
+
+
+# ---------------------------------------------------------------- power-of-two scales
+
+
+def _exponent(s):
+    """e with s == 2^e exactly (asserts s is a power of two)."""
+    m, e = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5), "scale is not a power of two"
+    return e - 1
+
+
+@pytest.mark.parametrize("name", list(INPUTS))
+def test_pow2_act_invariants(name):
+    x = INPUTS[name]
+    q, s = quant.quant_1x128(x, scale="pow2")
+    amax = np.abs(x.astype(np.float64)).reshape(x.shape[0], -1, 128).max(axis=2)
+    e = _exponent(s)
+    # amax / s lies in (224, 448]: exact comparisons (scaling by 2^e is exact)
+    assert np.all(np.ldexp(amax, -e) <= 448.0) and np.all(np.ldexp(amax, -e) > 224.0)
+    # the group's largest code sits in [0x76 (224), 0x7E (448)]; no NaN code
+    top = (q & 0x7F).reshape(x.shape[0], -1, 128).max(axis=2)
+    assert np.all((top >= 0x76) & (top <= 0x7E))
+    _qdq_check(x, q, np.repeat(s.astype(np.float64), 128, axis=1))
+
+
+def test_pow2_weight_invariants():
+    w = workloads.dense(seed=2, M=128, N=256, K=384)["w"].float().numpy()
+    q, s = quant.quant_128x128(w, scale="pow2")
+    e = _exponent(s)
+    amax = np.abs(w.astype(np.float64)).reshape(2, 128, 3, 128).max(axis=(1, 3))
+    assert np.all(np.ldexp(amax, -e) <= 448.0) and np.all(np.ldexp(amax, -e) > 224.0)
+    _qdq_check(w, q, np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1))
+
+
+def test_pow2_against_the_microscaling_floor_rule():
+    """Second derivation: the microscaling rule takes 2^(floor(log2 amax) - 8);
+    the pages' no-clipping rule needs one power of two more exactly when amax
+    exceeds 448 times that."""
+    for x in INPUTS.values():
+        _, s = quant.quant_1x128(x, scale="pow2")
+        amax = np.abs(x.astype(np.float64)).reshape(x.shape[0], -1, 128).max(axis=2)
+        ef = np.floor(np.log2(amax)) - 8
+        want = ef + (amax > 448.0 * np.exp2(ef))
+        assert np.array_equal(_exponent(s), want)
+
+
+def test_pow2_scale_brackets_the_amax_scale():
+    """amax/448 <= s < 2 * amax/448, so the fp32 amax scale s1 obeys s1 <= s <= 2 s1."""
+    x = INPUTS["normal_outliers"]
+    _, s1 = quant.quant_1x128(x)
+    _, s2 = quant.quant_1x128(x, scale="pow2")
+    assert np.all(s1 <= s2) and np.all(s2 <= 2 * s1)
+
+
+@pytest.mark.parametrize("j", [-5, 3])
+def test_pow2_equivariance(j):
+    x = INPUTS["student_t"]
+    q, s = quant.quant_1x128(x, scale="pow2")
+    q2, s2 = quant.quant_1x128(np.ldexp(x, j).astype(np.float32), scale="pow2")
+    assert np.array_equal(q, q2) and np.array_equal(s2, np.ldexp(s, j).astype(np.float32))
+    qn, sn = quant.quant_1x128(-x, scale="pow2")
+    assert np.array_equal(qn, q ^ 0x80) and np.array_equal(sn, s)
+
+
+def test_pow2_zero_group():
+    x = np.zeros((2, 256), np.float32)
+    x[1, 128:] = 1.0
+    x[0, 5] = -0.0
+    q, s = quant.quant_1x128(x, scale="pow2")
+    assert s[0].tolist() == [0.0, 0.0] and s[1, 0] == 0.0 and s[1, 1] == 2.0 ** -8
+    assert q[0, 5] == 0x80 and np.all(q[1, 128:] == 0x38 + (8 << 3))  # 1.0 * 2^8 = 256 -> 0x78
