@@ -11,10 +11,10 @@ events on its stream, and the quantisers are timed afterwards as batches.  The t
 inputs are rotated over three HBM copies so that the 256 MB last-level cache
 cannot serve the quantisers' reads from one step to the next.
 
-Other workloads (``--workload quant|moe|wgrad|dgrad``) measure the remaining rows of
+Other workloads (``--workload quant|moe|wgrad|dgrad|pow2``) measure the remaining rows of
 the path and print their own JSON line; the default run prints exactly one line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2]
                     [--no-cpu-baseline]
 """
 
@@ -221,6 +221,68 @@ def bench_dense(args, torch, fp8, workloads):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_dense(d)
     return out
+
+
+def bench_pow2(args, torch, fp8, workloads):
+    """The dense step with power-of-two scales: the quantisers write E8M0-valued
+    scales and the matrix cores apply them inside the scaled MFMA (no separate
+    promotion step)."""
+    M, N, K = 4096, 7168, 7168
+    d = workloads.dense()
+    xs = [d["x"].cuda() for _ in range(3)]
+    ws = [d["w"].cuda() for _ in range(3)]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    t_gemm = Timer(torch, args.steps)
+    t_act, t_w = Timer(torch, 1), Timer(torch, 1)
+
+    def step(i, timed):
+        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa, pow2=True)
+        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb, pow2=True)
+        if timed:
+            with t_gemm:
+                fp8.fp8_block_gemm(qa, sa, qb, sb, accum="scaled", y=y)
+        else:
+            fp8.fp8_block_gemm(qa, sa, qb, sb, accum="scaled", y=y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    with t_act:
+        for i in range(args.steps):
+            fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa, pow2=True)
+    with t_w:
+        for i in range(args.steps):
+            fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb, pow2=True)
+    torch.cuda.synchronize()
+    flop = 2.0 * M * N * K
+    gemm_ms = t_gemm.mean_ms()
+    act_bytes = M * K * (2 + 1) + M * (K // 128) * 4
+    w_bytes = N * K * (2 + 1) + (N // 128) * (K // 128) * 4
+    tf = flop / (gemm_ms * 1e-3) / 1e12
+    return {
+        "metric": "FP8 block-scaled GEMM TFLOP/s, power-of-two scales on the scaled MFMA", "value": flop / dt / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "dense projection with power-of-two (E8M0) group scales: quantise X bf16 [4096,7168] "
+                               "per 1x128 and W bf16 [7168,7168] per 128x128, scaled-MFMA GEMM Y = X W^T, bf16 out",
+                   "M": M, "N": N, "K": K, "accum": "scaled_mfma", "input_copies_rotated": 3},
+        "kernels": {
+            "fp8_quant_act_1x128_pow2": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
+            "fp8_quant_weight_128x128_pow2": _hbm_line("w", t_w.mean_ms() / args.steps, w_bytes, {}),
+            "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
+        },
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None},
+    }
 
 
 def cpu_baseline_dense(d):
@@ -504,7 +566,7 @@ def main():
     # The first ~100 dense GEMMs of a process run up to 25% slower while the
     # clocks ramp up; the default warm-up covers that ramp.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -525,7 +587,7 @@ def main():
     from fp8_fine_grained_amd import workloads
 
     fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
-          "dgrad": bench_dgrad}[args.workload]
+          "dgrad": bench_dgrad, "pow2": bench_pow2}[args.workload]
     out = fn(args, torch, fp8, workloads)
     print(json.dumps(out), flush=True)
 

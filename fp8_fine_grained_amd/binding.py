@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "fp8fg.h")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_HIP = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 B_BLOCK_128x128, B_ROW_1x128 = 0, 1
-ACCUM_FP8_MFMA, ACCUM_EXACT = 0, 1
+ACCUM_FP8_MFMA, ACCUM_EXACT, ACCUM_SCALED_MFMA = 0, 1, 2
 
 _lib = None
 
@@ -28,8 +28,12 @@ _c = ctypes
 _SIGS = {
     "fp8_quant_act_1x128": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
                             _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    "fp8_quant_act_1x128_pow2": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                 _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_quant_weight_128x128": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                  _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    "fp8_quant_weight_128x128_pow2": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
+                                      _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_quant_weight_128x128_dual": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
@@ -105,11 +109,12 @@ def _on_gpu(*ts):
             raise ValueError("all tensors must be on the GPU")
 
 
-def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
+def fp8_quant_act_1x128(x, q=None, scales=None, stream=None, pow2=False):
     """1x128 quantisation of the logical matrix ``x`` [M, K] along K.
 
     ``x`` may be row-contiguous, or a transposed view of a row-major [K, M]
     tensor (e.g. ``dy.t()``: tiles then run along the token axis).
+    ``pow2=True`` calls fp8_quant_act_1x128_pow2 (power-of-two scales).
     Returns ``(q uint8 [M, K], scales fp32 [M, K/128])``.
     """
     _on_gpu(x)
@@ -119,14 +124,16 @@ def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty((M, K // 128 if K % 128 == 0 else 0), dtype=torch.float32, device=x.device)
     _on_gpu(q, scales)
-    st = lib().fp8_quant_act_1x128(_ptr(x), _dtype_code(x.dtype), M, K, x.stride(0), x.stride(1),
-                                   _ptr(q), _ptr(scales), _stream(stream))
-    _check("fp8_quant_act_1x128", st)
+    fn = "fp8_quant_act_1x128_pow2" if pow2 else "fp8_quant_act_1x128"
+    st = getattr(lib(), fn)(_ptr(x), _dtype_code(x.dtype), M, K, x.stride(0), x.stride(1),
+                            _ptr(q), _ptr(scales), _stream(stream))
+    _check(fn, st)
     return q, scales
 
 
-def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
-    """128x128 quantisation of ``w`` [N, K].  Returns ``(q [N, K], scales [N/128, K/128])``."""
+def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None, pow2=False):
+    """128x128 quantisation of ``w`` [N, K].  Returns ``(q [N, K], scales [N/128, K/128])``.
+    ``pow2=True`` calls fp8_quant_weight_128x128_pow2 (power-of-two scales)."""
     _on_gpu(w)
     N, K = w.shape
     if w.stride(1) != 1:
@@ -136,9 +143,10 @@ def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
     _on_gpu(q, scales)
-    st = lib().fp8_quant_weight_128x128(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(q),
-                                        _ptr(scales), _stream(stream))
-    _check("fp8_quant_weight_128x128", st)
+    fn = "fp8_quant_weight_128x128_pow2" if pow2 else "fp8_quant_weight_128x128"
+    st = getattr(lib(), fn)(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(q),
+                            _ptr(scales), _stream(stream))
+    _check(fn, st)
     return q, scales
 
 
@@ -166,8 +174,8 @@ def fp8_quant_weight_128x128_dual(w, q=None, scales=None, q_t=None, scales_t=Non
 def _accum_code(accum, out_dtype):
     if accum is None:
         return ACCUM_EXACT if out_dtype == torch.float32 else ACCUM_FP8_MFMA
-    return {"fp8": ACCUM_FP8_MFMA, "exact": ACCUM_EXACT, ACCUM_FP8_MFMA: ACCUM_FP8_MFMA,
-            ACCUM_EXACT: ACCUM_EXACT}[accum]
+    return {"fp8": ACCUM_FP8_MFMA, "exact": ACCUM_EXACT, "scaled": ACCUM_SCALED_MFMA,
+            ACCUM_FP8_MFMA: ACCUM_FP8_MFMA, ACCUM_EXACT: ACCUM_EXACT, ACCUM_SCALED_MFMA: ACCUM_SCALED_MFMA}[accum]
 
 
 def _contig(*ts):
@@ -178,7 +186,8 @@ def _contig(*ts):
 
 def fp8_block_gemm(a, sa, b, sb, b_scale_mode="block", accum=None, out_dtype=torch.bfloat16,
                    y=None, stream=None):
-    """Y = deq(a) deq(b)^T; ``accum`` "fp8" or "exact" (default: exact for fp32 output)."""
+    """Y = deq(a) deq(b)^T; ``accum`` "fp8", "exact" (default for fp32 output) or
+    "scaled" (power-of-two scales applied by the matrix cores)."""
     _on_gpu(a, sa, b, sb)
     M, K = a.shape
     N = b.shape[0]

@@ -37,8 +37,12 @@ const char* fp8fg_status_string(int status) {
   }
 }
 
-int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
-                        int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m, int64_t stride_k, uint8_t* q,
+              float* scales, fp8fg_stream_t stream, bool pow2) {
   if (!valid_dtype(x_dtype) || M < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
   if (M == 0 || K == 0) return FP8FG_OK;
   if (K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
@@ -50,19 +54,19 @@ int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (stride_k == 1 && stride_m >= K) {
     if ((stride_m * es) % 16 != 0) return FP8FG_ERR_MISALIGNED;
-    return hip_status(fp8fg::launch_quant_act_rows(x, bf16, M, K, stride_m, q, scales, s));
+    return hip_status(fp8fg::launch_quant_act_rows(x, bf16, pow2, M, K, stride_m, q, scales, s));
   }
   if (stride_m == 1 && stride_k >= M) {
     if (M % 8 != 0) return FP8FG_ERR_UNSUPPORTED;
     if ((stride_k * es) % 16 != 0) return FP8FG_ERR_MISALIGNED;
-    return hip_status(fp8fg::launch_quant_act_cols(x, bf16, M, K, stride_k, q, scales, s));
+    return hip_status(fp8fg::launch_quant_act_cols(x, bf16, pow2, M, K, stride_k, q, scales, s));
   }
   if (stride_m < 0 || stride_k < 0) return FP8FG_ERR_INVALID_ARG;
   return FP8FG_ERR_UNSUPPORTED;
 }
 
-int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
-                             uint8_t* q, float* scales, fp8fg_stream_t stream) {
+int quant_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w, uint8_t* q, float* scales,
+                 fp8fg_stream_t stream, bool pow2) {
   if (!valid_dtype(w_dtype) || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
   if (N == 0 || K == 0) return FP8FG_OK;
   if (N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
@@ -71,8 +75,32 @@ int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, i
   if ((N / 128) * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 4) || (ld_w * elem_size(w_dtype)) % 16 != 0)
     return FP8FG_ERR_MISALIGNED;
-  return hip_status(fp8fg::launch_quant_weight(w, w_dtype == FP8FG_BF16, N, K, ld_w, q, scales,
+  return hip_status(fp8fg::launch_quant_weight(w, w_dtype == FP8FG_BF16, pow2, N, K, ld_w, q, scales,
                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                        int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  return quant_act(x, x_dtype, M, K, stride_m, stride_k, q, scales, stream, false);
+}
+
+int fp8_quant_act_1x128_pow2(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                             int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  return quant_act(x, x_dtype, M, K, stride_m, stride_k, q, scales, stream, true);
+}
+
+int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                             uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  return quant_weight(w, w_dtype, N, K, ld_w, q, scales, stream, false);
+}
+
+int fp8_quant_weight_128x128_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, float* scales, fp8fg_stream_t stream) {
+  return quant_weight(w, w_dtype, N, K, ld_w, q, scales, stream, true);
 }
 
 int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
@@ -96,7 +124,8 @@ namespace {
 int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                       int accum, const void* y, int y_dtype, int64_t M, int64_t N, int64_t K) {
   if (!valid_dtype(y_dtype) || M < 0 || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
-  if (accum != FP8FG_ACCUM_FP8_MFMA && accum != FP8FG_ACCUM_EXACT) return FP8FG_ERR_INVALID_ARG;
+  if (accum != FP8FG_ACCUM_FP8_MFMA && accum != FP8FG_ACCUM_EXACT && accum != FP8FG_ACCUM_SCALED_MFMA)
+    return FP8FG_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return -1;  // nothing to do
   if (K == 0 || K % 128 != 0 || N % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
   if (!a || !sa || !b || !sb || !y) return FP8FG_ERR_INVALID_ARG;
@@ -104,6 +133,19 @@ int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const
   if (!aligned(a, 16) || !aligned(b, 16) || !aligned(y, 16) || !aligned(sa, 4) || !aligned(sb, 4))
     return FP8FG_ERR_MISALIGNED;
   return FP8FG_OK;
+}
+
+fp8fg::GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* y,
+                          const int32_t* offsets, int64_t M, int64_t N, int64_t K, int64_t G, bool row_scales,
+                          int accum, int y_dtype) {
+  fp8fg::GemmArgs g{};
+  g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.y = y; g.offsets = offsets;
+  g.M = M; g.N = N; g.K = K; g.G = G;
+  g.row_scales = row_scales;
+  g.exact = accum == FP8FG_ACCUM_EXACT;
+  g.scaled = accum == FP8FG_ACCUM_SCALED_MFMA;
+  g.y_bf16 = y_dtype == FP8FG_BF16;
+  return g;
 }
 
 }  // namespace
@@ -118,9 +160,9 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const fl
   if (c != FP8FG_OK) return c;
   // launch grid: ceil(M/128) * (N/128) blocks
   if (((M + 127) / 128) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
-  fp8fg::GemmArgs g{a, sa, b, sb, y, nullptr, M, N, K, 1,
-                    b_scale_mode == FP8FG_B_ROW_1x128, accum == FP8FG_ACCUM_EXACT,
-                    y_dtype == FP8FG_BF16};
+  const fp8fg::GemmArgs g = gemm_args(a, sa, b, sb, y, nullptr, M, N, K, 1, b_scale_mode == FP8FG_B_ROW_1x128,
+                                      accum, y_dtype);
+  if (g.scaled && (g.row_scales || !fp8fg::fp8_block_kernel_applies(g))) return FP8FG_ERR_UNSUPPORTED;
   return hip_status(fp8fg::launch_block_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
@@ -135,8 +177,8 @@ int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* gro
   if (!group_offsets) return FP8FG_ERR_INVALID_ARG;
   if (!aligned(group_offsets, 4)) return FP8FG_ERR_MISALIGNED;
   if (G > kInt32Max || (M_total / 128 + G) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
-  fp8fg::GemmArgs g{a, sa, b, sb, y, group_offsets, M_total, N, K, G,
-                    false, accum == FP8FG_ACCUM_EXACT, y_dtype == FP8FG_BF16};
+  const fp8fg::GemmArgs g = gemm_args(a, sa, b, sb, y, group_offsets, M_total, N, K, G, false, accum, y_dtype);
+  if (g.scaled && !fp8fg::fp8_block_kernel_applies(g)) return FP8FG_ERR_UNSUPPORTED;
   return hip_status(fp8fg::launch_grouped_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
@@ -152,8 +194,9 @@ int fp8_block_grouped_gemm_gather(const uint8_t* a_tok, const float* sa_tok, int
   if (!aligned(group_offsets, 4) || !aligned(row_index, 4)) return FP8FG_ERR_MISALIGNED;
   if (G > kInt32Max || (M_total / 128 + G) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
   if (T > kInt32Max || T * K >= (int64_t(1) << 32)) return FP8FG_ERR_UNSUPPORTED;  // 32-bit row offsets
-  fp8fg::GemmArgs g{a_tok, sa_tok, b, sb, y, group_offsets, M_total, N, K, G,
-                    false, accum == FP8FG_ACCUM_EXACT, y_dtype == FP8FG_BF16, row_index, T};
+  fp8fg::GemmArgs g = gemm_args(a_tok, sa_tok, b, sb, y, group_offsets, M_total, N, K, G, false, accum, y_dtype);
+  g.row_index = row_index;
+  g.T = T;
   if (!fp8fg::fp8_block_kernel_applies(g)) return FP8FG_ERR_UNSUPPORTED;  // N % 256 != 0
   return hip_status(fp8fg::launch_grouped_gemm_gather(g, static_cast<hipStream_t>(stream)));
 }

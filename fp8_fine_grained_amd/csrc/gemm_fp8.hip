@@ -176,8 +176,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // every in-instruction sum exact); ROWS: one weight-side scale per row n and
 // K block instead of one per 128 x 128 block.
 // GATHER (grouped only): A rows and their scales are read through p.rows.
+// SCALED: power-of-two scales applied by the matrix cores (E8M0 operands of the
+// scaled MFMA), which also accumulate: no separate promotion step.
 template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED,
-          bool GATHER = false>
+          bool GATHER = false, bool SCALED = false>
 __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) {
   static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
   constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
@@ -197,6 +199,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   static_assert(STAGES >= 2, "at least double buffering");
   static_assert(!(ROWS && GROUPED), "grouped weights carry block scales");
   static_assert(!GATHER || GROUPED, "gathering is a grouped-GEMM mode");
+  static_assert(!SCALED || (!EXACT && !ROWS), "the scaled mode takes FP8 products and 128x128 weight scales");
   // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
   // padded by 16) in its own slice of the tile buffer.
   constexpr int EPI_PITCH = TN * 2 + 16;
@@ -472,6 +475,18 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   v8i fm[SM];
   float f[SM];
   v8i fn;
+  // Scaled mode: E8M0 codes (the fp32 exponent field) of the lane's act-row
+  // scale in each m sub-tile, and of the wavefront's weight-block scale.
+  int ex[SM];
+  int ew = 0;
+  auto e8m0 = [](float v) { return static_cast<int>((__float_as_uint(v) >> 23) & 0xFFu); };
+  auto act_scale = [&](int st, int j) { return s_sa[st][wm * TM + j * 16 + (lane & 15)]; };
+  auto wgt_scale = [&](int st) { return s_sb[st][((wn * TN) / 128) % SB_LEN]; };
+  // acc += 2^(ew-127) * 2^(ex-127) * (128-K FP8 partial), in one instruction; MFMA
+  // "A" is the weight fragment (scale per weight row), "B" the act fragment.
+  auto mma_scaled = [](const v8i& wfrag, const v8i& afrag, const v4f& c, int ewv, int exv) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfrag, afrag, c, 0, 0, 0, ewv, 0, exv);
+  };
   auto factor = [&](int st, int j) {
     const float a = s_sa[st][wm * TM + j * 16 + (lane & 15)];
     if constexpr (ROWS)
@@ -488,8 +503,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 #pragma unroll
     for (int j = 0; j < SM; ++j) {
       fm[j] = frag(tA, wm * TM + j * 16, lane);
-      f[j] = factor(0, j);
+      if constexpr (SCALED)
+        ex[j] = e8m0(act_scale(0, j));
+      else
+        f[j] = factor(0, j);
     }
+    if constexpr (SCALED) ew = e8m0(wgt_scale(0));
     fn = frag(tA + TILE_A, wn * TN, lane);
   }
 
@@ -555,11 +574,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       if (i == SN - 2) prefetch(clampkb(kb + PF));  // after this iteration's DMAs
       const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
       if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
-      WideFrag wn_frag;
-      if constexpr (EXACT) wn_frag = widen(fn);
+      if constexpr (SCALED) {
 #pragma unroll
-      for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
-      if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1]);
+        for (int j = 0; j < SM; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ew, ex[j]);
+      } else {
+        WideFrag wn_frag;
+        if constexpr (EXACT) wn_frag = widen(fn);
+#pragma unroll
+        for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
+        if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1]);
+      }
       fn = fn_next;
     }
     if constexpr (ROWS) sbr[(SN - 1) & 1] = row_scales(st, SN - 1);
@@ -572,6 +596,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     // the newest load, this iteration's prefetch, may stay in flight
     wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
     st = st == STAGES - 1 ? 0 : st + 1;
+    if constexpr (SCALED) {
+      const uint8_t* tA = tiles + st * STAGE;
+      const int ew_old = ew;
+#pragma unroll
+      for (int j = 0; j < SM; ++j) {
+        acc[SN - 1][j] = mma_scaled(fn, fm[j], acc[SN - 1][j], ew_old, ex[j]);
+        // (After the final block this reads a stage nobody uses; the values are dropped.)
+        fm[j] = frag(tA, wm * TM + j * 16, lane);
+        ex[j] = e8m0(act_scale(st, j));
+      }
+      ew = e8m0(wgt_scale(st));
+      fn = frag(tA + TILE_A, wn * TN, lane);
+      continue;
+    }
     float f_old[SM];
 #pragma unroll
     for (int j = 0; j < SM; ++j) f_old[j] = f[j];
@@ -643,7 +681,7 @@ template <int CFG> struct Cfg;
 template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
 
-template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER = false>
+template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using C = Cfg<CFG>;
   const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
@@ -651,15 +689,15 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
             static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN)};
   const unsigned blocks = static_cast<unsigned>(MT * p.NT);
   hipLaunchKernelGGL(
-      (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER>),
+      (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER, SCALED>),
       dim3(blocks), dim3(NTHREADS), 0, s, p);
   return hipGetLastError();
 }
 
-template <int CFG, bool EXACT, bool ROWS, bool GROUPED, bool GATHER = false>
+template <int CFG, bool EXACT, bool ROWS, bool GROUPED, bool GATHER = false, bool SCALED = false>
 hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
-  return g.y_bf16 ? launch_cfg<CFG, EXACT, ROWS, true, GROUPED, GATHER>(g, s)
-                  : launch_cfg<CFG, EXACT, ROWS, false, GROUPED, GATHER>(g, s);
+  return g.y_bf16 ? launch_cfg<CFG, EXACT, ROWS, true, GROUPED, GATHER, SCALED>(g, s)
+                  : launch_cfg<CFG, EXACT, ROWS, false, GROUPED, GATHER, SCALED>(g, s);
 }
 
 }  // namespace
@@ -674,13 +712,19 @@ bool fp8_block_kernel_applies(const GemmArgs& g) {
 // ~256 rows then waste less of their last m-tile).  The exact mode (fp16
 // operands, twice the fragment registers) and the row-scaled mode (one more
 // multiply and four row scales per sub-tile) use the 64 x 64 wavefront tile.
+// The scaled mode (power-of-two scales applied by the matrix cores) takes the
+// same tiles as the FP8 mode.
 hipError_t launch_grouped_gemm_gather(const GemmArgs& g, hipStream_t s) {
+  if (g.scaled) return launch_out<1, false, false, true, true, true>(g, s);
   return g.exact ? launch_out<1, true, false, true, true>(g, s) : launch_out<1, false, false, true, true>(g, s);
 }
 
 hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s) {
-  if (grouped)
+  if (grouped) {
+    if (g.scaled) return launch_out<1, false, false, true, false, true>(g, s);
     return g.exact ? launch_out<1, true, false, true>(g, s) : launch_out<1, false, false, true>(g, s);
+  }
+  if (g.scaled) return launch_out<0, false, false, false, false, true>(g, s);
   if (g.exact)
     return g.row_scales ? launch_out<1, true, true, false>(g, s) : launch_out<1, true, false, false>(g, s);
   return g.row_scales ? launch_out<1, false, true, false>(g, s) : launch_out<0, false, false, false>(g, s);

@@ -6,15 +6,16 @@
 
 namespace fp8fg {
 
+// pow2: power-of-two (E8M0) group scales instead of amax/448.
 // 1x128 quantisation, row-contiguous input (stride_k == 1).
-hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+hipError_t launch_quant_act_rows(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s);
 // 1x128 quantisation along K of a column-contiguous input (stride_m == 1):
 // x is physically [K, ld] row-major, element (m, k) at k*ld + m.
-hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+hipError_t launch_quant_act_cols(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s);
 // 128x128 quantisation.
-hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+hipError_t launch_quant_weight(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, int64_t ld,
                                uint8_t* q, float* scales, hipStream_t s);
 // 128x128 quantisation writing q [N,K] and the transposed q_t [K,N] (+ scales, scales_t).
 hipError_t launch_quant_weight_dual(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
@@ -30,6 +31,7 @@ struct GemmArgs {
   int64_t M, N, K, G;
   bool row_scales;  // B scales per row (1x128) instead of per 128x128 block
   bool exact;       // exact products (fp16 matrix cores) instead of FP8 MFMA
+  bool scaled;      // power-of-two scales applied by the matrix cores (E8M0), FP32 accumulation in the MFMA
   bool y_bf16;
   const int32_t* row_index = nullptr;  // grouped with gather: row r of A is a[row_index[r]]
   int64_t T = 0;                       // rows of a (and sa) when gathering

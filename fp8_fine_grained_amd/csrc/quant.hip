@@ -9,6 +9,15 @@
 // |x*inv| <= 448*(1+3*2^-24) < 464, so the hardware cvt, which rounds to
 // nearest even and maps [448, 464] to 448, never reaches its NaN range and
 // no explicit clamp is needed; zero groups give inv = 0 and codes 0x00/0x80.
+//
+// Power-of-two (E8M0) scales, for matrix cores that apply group scales
+// themselves (the microscaling formats the innerforce notes' Figure 7(a)
+// passage relates the grouping to; the group-scaled MMA of the tonho.wtf
+// wish list, "o que isso custou"): s = 2^e with e the smallest integer such
+// that amax <= 448 * 2^e, inv = 2^-e.  Writing amax = m * 2^E (m in [1, 2)),
+// amax / 2^(E-8) = 256 m is within 448 unless m > 1.75, so e = E - 8, plus one
+// when the mantissa field exceeds 0x600000 (m > 1.75).  x * inv is exact and
+// |x * inv| <= 448.
 #include "launch.h"
 
 namespace fp8fg {
@@ -21,9 +30,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+template <bool POW2 = false>
 __device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
-  s = amax / kE4M3Max;
-  inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+  if constexpr (!POW2) {
+    s = amax / kE4M3Max;
+    inv = (s == 0.0f) ? 0.0f : 1.0f / s;
+  } else {
+    const uint32_t b = __float_as_uint(amax);
+    int eb = static_cast<int>(b >> 23) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);  // biased exponent of s
+    eb = eb < 1 ? 1 : eb;  // amax below 448 * 2^-126 (outside the contract): the smallest normal scale
+    s = amax == 0.0f ? 0.0f : __uint_as_float(static_cast<uint32_t>(eb) << 23);
+    inv = amax == 0.0f ? 0.0f : __uint_as_float(static_cast<uint32_t>(254 - eb) << 23);
+  }
 }
 
 // Four fp32 values -> four E4M3 bytes (little-endian order a, b, c, d).
@@ -84,7 +102,7 @@ __device__ __forceinline__ void load16(const void* p, float (&v)[16]) {
 // ---------------------------------------------------------------- 1x128, rows
 // Eight lanes own one 1x128 tile (16 elements each); a 256-thread block
 // covers 32 consecutive tiles of the row-major [M, K/128] tile grid.
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restrict__ x, int64_t ld,
                                                              int G, int64_t tiles,
                                                              uint8_t* __restrict__ q,
@@ -106,7 +124,7 @@ __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restr
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   amax = max8(amax);
   float s, inv;
-  group_scale(amax, s, inv);
+  group_scale<POW2>(amax, s, inv);
   u32x4 out;
   out.x = cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
   out.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
@@ -134,7 +152,7 @@ __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restr
 constexpr int kColsTileBytes = 256;
 __device__ __forceinline__ int cols_swz(int row) { return ((row >> 4) & 7) << 1; }
 
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restrict__ x, int64_t ld,
                                                              int64_t M, int G, int CB,
                                                              uint8_t* __restrict__ q,
@@ -192,7 +210,7 @@ __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restr
   const int64_t m0 = col0 + static_cast<int64_t>(d) * COLS_PER_DW;
   if (m0 >= M) return;  // no cross-lane operations below
   float s0, inv0;
-  group_scale(amax0, s0, inv0);
+  group_scale<POW2>(amax0, s0, inv0);
   const int64_t k0 = row0 + 16 * tg;
   u32x4 o;
   o.x = cvt4(lo(w[0]) * inv0, lo(w[1]) * inv0, lo(w[2]) * inv0, lo(w[3]) * inv0);
@@ -203,7 +221,7 @@ __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restr
   if (tg == 0) scales[m0 * G + g] = s0;
   if constexpr (BF16) {
     float s1, inv1;
-    group_scale(amax1, s1, inv1);
+    group_scale<POW2>(amax1, s1, inv1);
     u32x4 h;
     h.x = cvt4(bf16_hi(w[0]) * inv1, bf16_hi(w[1]) * inv1, bf16_hi(w[2]) * inv1, bf16_hi(w[3]) * inv1);
     h.y = cvt4(bf16_hi(w[4]) * inv1, bf16_hi(w[5]) * inv1, bf16_hi(w[6]) * inv1, bf16_hi(w[7]) * inv1);
@@ -217,7 +235,7 @@ __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restr
 // ---------------------------------------------------------------- 128x128
 // One 256-thread block per 128x128 block, read from HBM once: thread t holds
 // columns 8*(t%16) .. +7 of rows t/16 + 16*i (i = 0..7) in registers.
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ void __launch_bounds__(256) quant_weight_kernel(const void* __restrict__ w, int64_t ld,
                                                            int GK, uint8_t* __restrict__ q,
                                                            float* __restrict__ scales, int64_t K) {
@@ -257,7 +275,7 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const void* __restric
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   float s, inv;
-  group_scale(amax, s, inv);
+  group_scale<POW2>(amax, s, inv);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = static_cast<int64_t>(bi) * 128 + r0 + 16 * i;
@@ -377,39 +395,42 @@ __global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __re
 
 }  // namespace
 
-hipError_t launch_quant_act_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+hipError_t launch_quant_act_rows(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s) {
   const int G = static_cast<int>(K / 128);
   const int64_t tiles = M * G;
   const dim3 grid(static_cast<unsigned>((tiles + 31) / 32));
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, K); };
   if (bf16)
-    hipLaunchKernelGGL(quant_act_rows_kernel<true>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, K);
+    pow2 ? go(quant_act_rows_kernel<true, true>) : go(quant_act_rows_kernel<true, false>);
   else
-    hipLaunchKernelGGL(quant_act_rows_kernel<false>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, K);
+    pow2 ? go(quant_act_rows_kernel<false, true>) : go(quant_act_rows_kernel<false, false>);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_act_cols(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld,
+hipError_t launch_quant_act_cols(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s) {
   const int G = static_cast<int>(K / 128);
   const int tile_cols = kColsTileBytes / (bf16 ? 2 : 4);
   const int CB = static_cast<int>((M + tile_cols - 1) / tile_cols);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(CB) * G));
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(512), 0, s, x, ld, M, G, CB, q, scales, K); };
   if (bf16)
-    hipLaunchKernelGGL(quant_act_cols_kernel<true>, grid, dim3(512), 0, s, x, ld, M, G, CB, q, scales, K);
+    pow2 ? go(quant_act_cols_kernel<true, true>) : go(quant_act_cols_kernel<true, false>);
   else
-    hipLaunchKernelGGL(quant_act_cols_kernel<false>, grid, dim3(512), 0, s, x, ld, M, G, CB, q, scales, K);
+    pow2 ? go(quant_act_cols_kernel<false, true>) : go(quant_act_cols_kernel<false, false>);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_weight(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+hipError_t launch_quant_weight(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, int64_t ld,
                                uint8_t* q, float* scales, hipStream_t s) {
   const int GK = static_cast<int>(K / 128);
   const dim3 grid(static_cast<unsigned>((N / 128) * GK));
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, w, ld, GK, q, scales, K); };
   if (bf16)
-    hipLaunchKernelGGL(quant_weight_kernel<true>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
+    pow2 ? go(quant_weight_kernel<true, true>) : go(quant_weight_kernel<true, false>);
   else
-    hipLaunchKernelGGL(quant_weight_kernel<false>, grid, dim3(256), 0, s, w, ld, GK, q, scales, K);
+    pow2 ? go(quant_weight_kernel<false, true>) : go(quant_weight_kernel<false, false>);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 3
+#define FP8FG_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum {
@@ -82,7 +82,19 @@ enum {
   /* FP8 operands widened exactly to fp16 on chip and multiplied on the fp16
    * matrix cores: every product is exact and sums are FP32.  Half rate.  Use
    * when the output is FP32 and FP32-level agreement is required. */
-  FP8FG_ACCUM_EXACT = 1
+  FP8FG_ACCUM_EXACT = 1,
+  /* Power-of-two scales only (as written by the *_pow2 quantisers): the
+   * scales enter the matrix-core instruction as E8M0 exponents (the
+   * group-scaled MMA on the tonho.wtf page's wish list, "o que isso custou";
+   * the microscaling formats of the innerforce notes' Figure 7(a) passage).
+   * Products within a K block are summed as in FP8FG_ACCUM_FP8_MFMA, scaled
+   * exactly by 2^(ea+eb), and added to the FP32 accumulator inside the same
+   * instruction, so there is no separate promotion step.  Requires
+   * FP8FG_B_BLOCK_128x128 and N % 256 == 0 (FP8FG_ERR_UNSUPPORTED otherwise).
+   * A scale that is not a power of two is read as 2^(its fp32 exponent):
+   * unspecified results, never a fault.  Zero scales (all-zero groups) are
+   * fine: their codes are zero. */
+  FP8FG_ACCUM_SCALED_MFMA = 2
 };
 
 /* A hipStream_t passed as an opaque pointer; NULL is the default stream. */
@@ -112,6 +124,18 @@ int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_
                         int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream);
 
 /*
+ * The same with power-of-two group scales (for FP8FG_ACCUM_SCALED_MFMA).  The
+ * microscaling reading of the innerforce notes' Figure 7(a) passage: per group
+ *     s = 2^e, e the smallest integer with amax <= 448 * 2^e  (0 if amax == 0),
+ *     q = E4M3_RNE(fl32(x * 2^-e))       (exact scaling; |x * 2^-e| <= 448)
+ * so the largest code of a nonzero group lies in [0x76, 0x7E].  Arguments,
+ * layouts and requirements as fp8_quant_act_1x128; amax must be 0 or at least
+ * 448 * 2^-126.
+ */
+int fp8_quant_act_1x128_pow2(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
+                             int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream);
+
+/*
  * 128x128 weight quantisation (same passages).
  *
  * w       [N, K] of `w_dtype`, row pitch ld_w >= K elements; W is [out, in]:
@@ -123,6 +147,10 @@ int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_
  */
 int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                              uint8_t* q, float* scales, fp8fg_stream_t stream);
+
+/* The same with power-of-two block scales (rule as fp8_quant_act_1x128_pow2). */
+int fp8_quant_weight_128x128_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, float* scales, fp8fg_stream_t stream);
 
 /*
  * 128x128 weight quantisation that also writes the transposed operand, for the

@@ -20,7 +20,8 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
-    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_quant_weight_128x128_dual",
+    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
+                          "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual",
                           "fp8_block_gemm", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
                           "fp8fg_status_string", "fp8fg_abi_version"}
     for n in names:
@@ -28,14 +29,15 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 3
+    assert L.fp8fg_abi_version() == 4
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
 
 
-def test_quant_act_validation(L):
-    f = L.fp8_quant_act_1x128
+@pytest.mark.parametrize("fn", ["fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2"])
+def test_quant_act_validation(L, fn):
+    f = getattr(L, fn)
     assert f(GOOD, 7, 4, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG  # dtype
     assert f(GOOD, fp8.BF16, -1, 128, 128, 1, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG
     assert f(NULL, fp8.BF16, 0, 128, 128, 1, NULL, NULL, NULL) == fp8.OK  # M == 0: no-op
@@ -48,8 +50,9 @@ def test_quant_act_validation(L):
     assert f(GOOD, fp8.BF16, 12, 128, 1, 16, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED  # transposed, M % 8
 
 
-def test_quant_weight_validation(L):
-    f = L.fp8_quant_weight_128x128
+@pytest.mark.parametrize("fn", ["fp8_quant_weight_128x128", "fp8_quant_weight_128x128_pow2"])
+def test_quant_weight_validation(L, fn):
+    f = getattr(L, fn)
     assert f(GOOD, fp8.BF16, 100, 128, 128, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED
     assert f(GOOD, fp8.BF16, 128, 130, 130, GOOD, GOOD, NULL) == fp8.ERR_UNSUPPORTED
     assert f(GOOD, fp8.BF16, 128, 128, 64, GOOD, GOOD, NULL) == fp8.ERR_INVALID_ARG  # ld < K
@@ -92,6 +95,10 @@ def test_gemm_validation(L):
     assert f(*args(sb=NULL)) == fp8.ERR_INVALID_ARG
     assert f(*args(y=BAD)) == fp8.ERR_MISALIGNED
     assert f(*args(sa=ctypes.c_void_p(0x10001))) == fp8.ERR_MISALIGNED
+    # power-of-two scales on the matrix cores: 128x128 B scales and N % 256 == 0 only
+    assert f(*args(accum=fp8.ACCUM_SCALED_MFMA)) == fp8.ERR_UNSUPPORTED  # N = 128
+    assert f(*args(accum=fp8.ACCUM_SCALED_MFMA, N=256, mode=fp8.B_ROW_1x128)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(accum=fp8.ACCUM_SCALED_MFMA, a=NULL, M=0)) == fp8.OK
 
 
 def test_grouped_validation(L):
