@@ -136,6 +136,12 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32
 // issued (no branch around it), so every wavefront's count of outstanding
 // loads per stage stays the same whatever the mask.
 __device__ __forceinline__ void dma16_masked(const uint8_t* base, uint32_t voff, uint32_t lds, uint64_t mask) {
+  // (the mask is wave-uniform; readfirstlane keeps it in scalar registers.  Its
+  // int results are widened as uint32: a sign-extended low word would switch on
+  // lanes 32-63 whenever lane 31 is live.)
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(mask >> 32)));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(mask)));
+  mask = (static_cast<uint64_t>(hi) << 32) | lo;
   uint64_t saved;
   asm volatile(
       "s_mov_b64 %0, exec\n\t"
@@ -184,15 +190,25 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
   constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
   constexpr int SM = TM / 16, SN = TN / 16;
-  static_assert(ROWS || TN % 128 == 0 || 128 % TN == 0, "a wavefront's n range lies in one weight block");
+  // BALIGN: tiles start on weight-block boundaries and a wavefront's n range lies
+  // in one weight block, so one block factor serves the wavefront; otherwise
+  // (224-wide tiles) each 16-wide sub-tile takes the factor of its own block.
+  constexpr bool BALIGN = BN % 128 == 0 && (TN % 128 == 0 || 128 % TN == 0);
+  static_assert(ROWS || BALIGN || (BN % 32 == 0 && !GROUPED), "unaligned weight tiles: dense, 32-row multiples");
   constexpr int TILE_A = BM * 128;
   constexpr int TILE_B = BN * 128;
   constexpr int STAGE = TILE_A + TILE_B;
-  constexpr int A_DMA = BM / 64, B_DMA = BN / 64;  // 8-row DMAs per wavefront per stage
+  // 8-row DMAs per wavefront per stage.  B row groups are dealt out in
+  // contiguous runs when they divide evenly over the 8 wavefronts, else
+  // round-robin (group w + 8d for DMA d), the missing last ones masked off.
+  constexpr int B_GROUPS = BN / 8;
+  constexpr bool B_RR = B_GROUPS % 8 != 0;
+  constexpr int A_DMA = BM / 64, B_DMA = (B_GROUPS + 7) / 8;
   constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales (64 rows each)
   constexpr int SB_WAVES = ROWS ? BN / 64 : 1;       // and the B scales (64 rows, or all blocks)
   static_assert(SA_WAVES + SB_WAVES <= 8, "one scale DMA per wavefront");
   constexpr int SB_LEN = ROWS ? BN : 64;
+  constexpr int NB = BALIGN ? BN / 128 : BN / 128 + 2;  // weight blocks a tile can touch (block mode)
   // loads per wavefront per stage: tiles + one scale (or filler) DMA
   constexpr int LOADS = A_DMA + B_DMA + 1;
   constexpr int WAIT_N = (STAGES - 2) * LOADS;
@@ -355,7 +371,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // are folded into the wave-uniform base.  Gathered rows keep one offset per DMA.
   const int uw = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + (row_lo + uw * (BM / 8)) * p.K);
-  const uint8_t* b_base = uniform_ptr(bmat + (n0 + uw * (BN / 8)) * p.K);
+  const uint8_t* b_base = uniform_ptr(bmat + (n0 + uw * (B_RR ? 8 : BN / 8)) * p.K);
   const uint32_t voff = static_cast<uint32_t>(lrow * p.K + lchunk);
   uint32_t va[GATHER ? A_DMA : 1];
   uint64_t a_live[A_DMA];  // lanes whose tile row lies inside the segment (or the matrix)
@@ -377,13 +393,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     w = w < SB_WAVES ? w : 0;  // filler wavefronts re-read the first weight rows' scales
     gs = bscale + (n0 + w * 64 + lane) * p.KB;
   } else {
-    const int blk = lane < BN / 128 - 1 ? lane : BN / 128 - 1;
-    gs = bscale + (n0 / 128 + blk) * p.KB;
+    int64_t blk = n0 / 128 + (lane < NB - 1 ? lane : NB - 1);
+    blk = blk < p.N / 128 ? blk : p.N / 128 - 1;
+    gs = bscale + blk * p.KB;
   }
   // wave-uniform LDS destinations (readfirstlane tells the compiler they are scalar)
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / 8) * 128;
-  const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (BN / 8) * 128;
+  const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (B_RR ? 8 : BN / 8) * 128;
   const bool b_scale_wave = uwave >= SA_WAVES && uwave < SA_WAVES + SB_WAVES;
   const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
                           : (b_scale_wave ? lds_addr(&s_sb[0][(uwave - SA_WAVES) * 64]) : lds_addr(s_filler));
@@ -399,7 +416,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // touches one slice, 32 A rows and 64 B rows, and each line is requested
   // about once per XCD.  The loads land in the scratch slot, never read.
   constexpr int PF_DIST = 3;
-  constexpr int PF = (GROUPED || BM + BN != NTHREADS) ? 0 : PF_DIST;
+  constexpr int PF = (GROUPED || BM != 256) ? 0 : PF_DIST;
   const uint8_t* pf_ptr = nullptr;
   if constexpr (PF > 0) {
     const int live = static_cast<int>(row_hi - row_lo);
@@ -409,14 +426,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       r = r < live ? r : live - 1;
       pf_ptr = p.a + (row_lo + r) * p.K;
     } else {
-      pf_ptr = bmat + (n0 + (mt % 4) * (BN / 4) + (slot - BM / 8)) * p.K;
+      pf_ptr = bmat + (n0 + (mt % 4) * (BN / 4) + (slot - BM / 8) % (BN / 4)) * p.K;
     }
   }
   auto prefetch = [&](int kb) {
     if constexpr (PF > 0) dma4(pf_ptr + static_cast<int64_t>(kb) * 128, lds_addr(s_filler));
   };
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
-  constexpr int SPREAD = SN >= 8 ? 6 : (SN >= 4 ? SN / 2 : SN);  // sub-tile steps that issue them
+  constexpr int SPREAD = SN >= 7 ? SN - 2 : (SN >= 4 ? SN / 2 : SN);  // sub-tile steps that issue them
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
@@ -425,8 +442,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
         dma16_masked(a_base + kof, va[d], lds_ta + so + d * 1024, a_live[d]);
       else
         dma16_masked(a_base + kof + static_cast<int64_t>(d) * 8 * p.K, voff, lds_ta + so + d * 1024, a_live[d]);
-    } else {
+    } else if constexpr (!B_RR) {
       dma16(b_base + kof + static_cast<int64_t>(d - A_DMA) * 8 * p.K, voff, lds_tb + so + (d - A_DMA) * 1024);
+    } else {
+      const int db = d - A_DMA;
+      dma16_masked(b_base + kof + static_cast<int64_t>(db) * 64 * p.K, voff, lds_tb + so + db * 8 * 1024,
+                   uw + 8 * db < B_GROUPS ? ~0ull : 0ull);
     }
   };
   auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
@@ -489,11 +510,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   };
   auto factor = [&](int st, int j) {
     const float a = s_sa[st][wm * TM + j * 16 + (lane & 15)];
-    if constexpr (ROWS)
+    if constexpr (ROWS || !BALIGN)
       return a;
     else
       return a * s_sb[st][(wn * TN) / 128];
   };
+  // Unaligned weight tiles: the block scale of n sub-tile i (staged blocks start
+  // at block n0/128).
+  const int n0_in_blk = static_cast<int>(n0 % 128);
+  auto sub_scale = [&](int st, int i) { return s_sb[st][((n0_in_blk + wn * TN + i * 16) / 128) % SB_LEN]; };
+  float sbv[BALIGN ? 1 : SN];
   // Row mode: the 4 weight-row scales of this lane in n sub-tile i.
   auto row_scales = [&](int st, int i) {
     return *reinterpret_cast<const v4f*>(&s_sb[st][(wn * TN + i * 16 + 4 * (lane >> 4)) % SB_LEN]);
@@ -527,18 +553,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       return r;
     }
   };
-  // acc[i] += P * factor, with the row scales of sub-tile i in row mode.
-  auto promote = [&](v4f (&a)[SM], const v4f (&P)[SM], const float (&fv)[SM], const v4f& sbr) {
+  // acc[i] += P * factor, with the row scales of sub-tile i in row mode, or the
+  // block scale bs of sub-tile i for unaligned weight tiles.
+  auto promote = [&](v4f (&a)[SM], const v4f (&P)[SM], const float (&fv)[SM], const v4f& sbr, float bs) {
 #pragma unroll
-    for (int j = 0; j < SM; ++j)
+    for (int j = 0; j < SM; ++j) {
+      const float fj = BALIGN ? fv[j] : fv[j] * bs;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if constexpr (ROWS)
           a[j][r] = fmaf(P[j][r] * sbr[r], fv[j], a[j][r]);
         else
-          a[j][r] = fmaf(P[j][r], fv[j], a[j][r]);
+          a[j][r] = fmaf(P[j][r], fj, a[j][r]);
       }
+    }
   };
+  auto bsv = [&](int i) { if constexpr (BALIGN) return 0.0f; else return sbv[i]; };
 
   int st = 0;  // stage holding block kb
   v4f P[2][SM];
@@ -550,6 +580,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     const int st_fill = st == 0 ? STAGES - 1 : st - 1;
     const int kb_fill = clampkb(kb + STAGES - 1);
     const uint8_t* tB = tiles + st * STAGE + TILE_A;
+    if constexpr (!BALIGN) {
+#pragma unroll
+      for (int i = 0; i < SN; ++i) sbv[i] = sub_scale(st, i);
+    }
     if constexpr (EXACT) {
 #pragma unroll
       for (int j = 0; j < SM; ++j) wm_frag[j] = widen(fm[j]);
@@ -575,14 +609,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       const v8i fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
       if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
       if constexpr (SCALED) {
+        const int ewi = BALIGN ? ew : e8m0(bsv(i));
 #pragma unroll
-        for (int j = 0; j < SM; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ew, ex[j]);
+        for (int j = 0; j < SM; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
       } else {
         WideFrag wn_frag;
         if constexpr (EXACT) wn_frag = widen(fn);
 #pragma unroll
         for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
-        if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1]);
+        if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
       }
       fn = fn_next;
     }
@@ -598,7 +633,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     st = st == STAGES - 1 ? 0 : st + 1;
     if constexpr (SCALED) {
       const uint8_t* tA = tiles + st * STAGE;
-      const int ew_old = ew;
+      const int ew_old = BALIGN ? ew : e8m0(bsv(SN - 1));
 #pragma unroll
       for (int j = 0; j < SM; ++j) {
         acc[SN - 1][j] = mma_scaled(fn, fm[j], acc[SN - 1][j], ew_old, ex[j]);
@@ -626,8 +661,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       }
       fn = frag(tA + TILE_A, wn * TN, lane);
     }
-    promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1]);
-    promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1]);
+    promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
+    promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
@@ -651,13 +686,15 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
     // (ds ops of one wavefront complete in order: no barrier needed here)
     constexpr int LANES_PER_ROW = TN * 2 / 16;
     constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+    static_assert(TM % ROWS_PER_PASS == 0, "whole passes");
     const int c16 = lane % LANES_PER_ROW;
+    const bool epi_lane = lane < ROWS_PER_PASS * LANES_PER_ROW;
 #pragma unroll
     for (int pass = 0; pass < TM / ROWS_PER_PASS; ++pass) {
-      const int mr = pass * ROWS_PER_PASS + lane / LANES_PER_ROW;
+      const int mr = pass * ROWS_PER_PASS + (epi_lane ? lane / LANES_PER_ROW : 0);
       const int64_t m = row_lo + wm * TM + mr;
       const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * EPI_PITCH + c16 * 16);
-      if (m < row_hi)
+      if (epi_lane && m < row_hi)
         *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + m * p.N + n0 + wn * TN + c16 * 8) = v;
     }
   } else {
@@ -677,9 +714,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
 // Tile configurations: {BM, BN, WM, WN, STAGES}.
 //   0: 256 x 256, 4 x 2 wavefronts (64 x 128 each), 2 stages (128 KB LDS)
 //   1: 128 x 256, 2 x 4 wavefronts (64 x 64 each), 3 stages (144 KB LDS)
+//   2: 256 x 224, 4 x 2 wavefronts (64 x 112 each), 2 stages (120 KB LDS)
 template <int CFG> struct Cfg;
 template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
+template <> struct Cfg<2> { static constexpr int BM = 256, BN = 224, WM = 4, WN = 2, ST = 2; };
 
 template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
@@ -704,8 +743,23 @@ hipError_t launch_out(const GemmArgs& g, hipStream_t s) {
 
 bool fp8_block_kernel_applies(const GemmArgs& g) {
   // (the DMA lane offsets are 32-bit: 256 rows x K bytes must stay below 4 GiB)
-  return g.N % 256 == 0 && g.K < (int64_t(1) << 24);
+  if (g.K >= (int64_t(1) << 24)) return false;
+  if (g.N % 256 == 0) return true;
+  // 224-wide tiles: dense, 128x128 weight scales, FP8 or scaled accumulation
+  return g.N % 224 == 0 && g.offsets == nullptr && !g.exact && !g.row_scales;
 }
+
+namespace {
+
+// Width of the 256-row dense tiles: 256 whenever N allows it, else 224.
+// Measured on 4096 x 7168 x 7168, 224-wide tiles (512 tiles, exactly two
+// rounds of the 256 CUs) run 5-8% slower than 256-wide ones (448 tiles, 1.75
+// rounds): the per-block costs (barrier, A fragments, scales) are spread over
+// 7/8 of the MFMAs, and the last round of 256-wide tiles runs on a partly idle
+// chip at a higher clock.  So 224 serves only N that 256 does not divide.
+int dense_tile_width(const GemmArgs& g) { return g.N % 256 == 0 ? 256 : 224; }
+
+}  // namespace
 
 // Block-scaled FP8 accumulation: dense GEMMs use the 256 x 256 tile (least L2
 // and LDS traffic per flop), grouped GEMMs the 128-row tile (expert segments of
@@ -724,10 +778,14 @@ hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s)
     if (g.scaled) return launch_out<1, false, false, true, false, true>(g, s);
     return g.exact ? launch_out<1, true, false, true>(g, s) : launch_out<1, false, false, true>(g, s);
   }
-  if (g.scaled) return launch_out<0, false, false, false, false, true>(g, s);
   if (g.exact)
     return g.row_scales ? launch_out<1, true, true, false>(g, s) : launch_out<1, true, false, false>(g, s);
-  return g.row_scales ? launch_out<1, false, true, false>(g, s) : launch_out<0, false, false, false>(g, s);
+  if (g.row_scales) return launch_out<1, false, true, false>(g, s);
+  const bool narrow = dense_tile_width(g) == 224;
+  if (g.scaled)
+    return narrow ? launch_out<2, false, false, false, false, true>(g, s)
+                  : launch_out<0, false, false, false, false, true>(g, s);
+  return narrow ? launch_out<2, false, false, false>(g, s) : launch_out<0, false, false, false>(g, s);
 }
 
 }  // namespace fp8fg

@@ -49,7 +49,8 @@ def test_tiny_fp32_exact_and_fp8():
     check_bf16(_run(g, 128, 128, torch.bfloat16, "fp8"), ref, "bf16 out")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (1, 128, 128), (129, 256, 384), (64, 128, 7168)])
+@pytest.mark.parametrize("M,N,K", [(300, 384, 1024), (1, 128, 128), (129, 256, 384), (64, 128, 7168),
+                                   (300, 896, 1024), (129, 2688, 384)])  # N % 256 != 0: 224-wide tiles
 def test_dense_shapes_bf16(M, N, K):
     d = workloads.dense(M=M, N=N, K=K)
     g, r = _quantised(d["x"], d["w"])

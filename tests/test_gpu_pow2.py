@@ -87,7 +87,8 @@ def _gemm(g, M, N, dtype):
     return y
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 256, 1024), (129, 512, 384), (1, 256, 128), (64, 256, 7168)])
+@pytest.mark.parametrize("M,N,K", [(300, 256, 1024), (129, 512, 384), (1, 256, 128), (64, 256, 7168),
+                                   (300, 896, 1024), (129, 2688, 384)])  # N % 256 != 0: 224-wide tiles
 def test_scaled_gemm_shapes(M, N, K):
     d = workloads.dense(M=M, N=N, K=K)
     g, r = _operands(d["x"], d["w"])
