@@ -36,6 +36,8 @@ Modules:
 * :mod:`oracle.gemm`  -- fp64 GEMM on the dequantised operands, dense and
   grouped (per-expert row segments), plus row-sampled variants for checking
   full-size outputs.
+* :mod:`oracle.ablation` -- per-tensor scaling (the practice the grouping
+  replaces) against 1x128 / 128x128 groups: quantisation and GEMM error.
 
 Every function here is plain numpy in the precision the method states
 (fp32 for the scale/cast steps, where the result must be bit-exact) or fp64
@@ -43,4 +45,4 @@ Every function here is plain numpy in the precision the method states
 docstring; all are pinned by ``tests/test_oracle_*.py``.
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import e4m3, quant, gemm, ablation  # noqa: F401
