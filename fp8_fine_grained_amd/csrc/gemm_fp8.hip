@@ -7,7 +7,8 @@
 // section 2.2.3; tonho.wtf "DeepSeek-V3", "como funciona").
 //
 // Layout on gfx950:
-//  * 512-thread workgroups (8 wavefronts, 2 per SIMD), each wavefront owning a
+//  * 512-thread workgroups (8 wavefronts, 2 per SIMD; the template also takes 4,
+//    one per SIMD, which measured 4% slower on the grouped GEMM), each wavefront owning a
 //    (TN x TM) block of 16 x 16 sub-tiles.  Two tile shapes:
 //      dense   256 (m) x 256 (n), wavefronts 4 (m) x 2 (n) of 64 x 128, 2 stages;
 //      grouped 128 (m) x 256 (n), wavefronts 2 (m) x 4 (n) of 64 x 64, 3 stages
@@ -59,7 +60,6 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int NTHREADS = 512;  // 8 wavefronts, 2 per SIMD
 constexpr int GROUP_M = 4;     // m-tiles per band in the dense tile order
 
 struct FParams {
@@ -186,8 +186,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // scaled MFMA), which also accumulate: no separate promotion step.
 template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED,
           bool GATHER = false, bool SCALED = false>
-__global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) {
-  static_assert(WM * WN * 64 == NTHREADS, "8 wavefronts");
+__global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams p) {
+  constexpr int NW = WM * WN;  // wavefronts: 8 (2 per SIMD) or 4 (1 per SIMD)
+  static_assert(NW == 8 || NW == 4, "8 or 4 wavefronts");
   constexpr int TM = BM / WM, TN = BN / WN;  // wavefront tile (m, n)
   constexpr int SM = TM / 16, SN = TN / 16;
   // BALIGN: tiles start on weight-block boundaries and a wavefront's n range lies
@@ -202,11 +203,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // contiguous runs when they divide evenly over the 8 wavefronts, else
   // round-robin (group w + 8d for DMA d), the missing last ones masked off.
   constexpr int B_GROUPS = BN / 8;
-  constexpr bool B_RR = B_GROUPS % 8 != 0;
-  constexpr int A_DMA = BM / 64, B_DMA = (B_GROUPS + 7) / 8;
+  constexpr bool B_RR = B_GROUPS % NW != 0;
+  static_assert(BM % (8 * NW) == 0, "whole A DMAs per wavefront");
+  constexpr int A_DMA = BM / 8 / NW, B_DMA = (B_GROUPS + NW - 1) / NW;
   constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales (64 rows each)
   constexpr int SB_WAVES = ROWS ? BN / 64 : 1;       // and the B scales (64 rows, or all blocks)
-  static_assert(SA_WAVES + SB_WAVES <= 8, "one scale DMA per wavefront");
+  static_assert(SA_WAVES + SB_WAVES <= NW, "one scale DMA per wavefront");
   constexpr int SB_LEN = ROWS ? BN : 64;
   constexpr int NB = BALIGN ? BN / 128 : BN / 128 + 2;  // weight blocks a tile can touch (block mode)
   // loads per wavefront per stage: tiles + one scale (or filler) DMA
@@ -219,7 +221,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
   // padded by 16) in its own slice of the tile buffer.
   constexpr int EPI_PITCH = TN * 2 + 16;
-  constexpr int EPI_BYTES = 8 * TM * EPI_PITCH;
+  constexpr int EPI_BYTES = NW * TM * EPI_PITCH;
   constexpr int TILES_BYTES = STAGES * STAGE > EPI_BYTES ? STAGES * STAGE : EPI_BYTES;
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[TILES_BYTES];
   __shared__ __attribute__((aligned(16))) float s_sa[STAGES][BM];
@@ -370,14 +372,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // (row lrow, chunk lchunk); the wavefront's row block and the DMA's 8-row step
   // are folded into the wave-uniform base.  Gathered rows keep one offset per DMA.
   const int uw = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + (row_lo + uw * (BM / 8)) * p.K);
-  const uint8_t* b_base = uniform_ptr(bmat + (n0 + uw * (B_RR ? 8 : BN / 8)) * p.K);
+  const uint8_t* a_base = uniform_ptr(GATHER ? p.a : p.a + (row_lo + uw * (BM / NW)) * p.K);
+  const uint8_t* b_base = uniform_ptr(bmat + (n0 + uw * (B_RR ? 8 : BN / NW)) * p.K);
   const uint32_t voff = static_cast<uint32_t>(lrow * p.K + lchunk);
   uint32_t va[GATHER ? A_DMA : 1];
   uint64_t a_live[A_DMA];  // lanes whose tile row lies inside the segment (or the matrix)
 #pragma unroll
   for (int i = 0; i < A_DMA; ++i) {
-    const int r = wave * (BM / 8) + i * 8 + lrow;
+    const int r = wave * (BM / NW) + i * 8 + lrow;
     int64_t row = row_lo + r;
     a_live[i] = __ballot(row < row_hi);
     row = row < row_hi ? row : row_hi - 1;
@@ -399,8 +401,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   }
   // wave-uniform LDS destinations (readfirstlane tells the compiler they are scalar)
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / 8) * 128;
-  const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (B_RR ? 8 : BN / 8) * 128;
+  const uint32_t lds_ta = lds_addr(tiles) + uwave * (BM / NW) * 128;
+  const uint32_t lds_tb = lds_addr(tiles) + TILE_A + uwave * (B_RR ? 8 : BN / NW) * 128;
   const bool b_scale_wave = uwave >= SA_WAVES && uwave < SA_WAVES + SB_WAVES;
   const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
                           : (b_scale_wave ? lds_addr(&s_sb[0][(uwave - SA_WAVES) * 64]) : lds_addr(s_filler));
@@ -416,7 +418,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
   // touches one slice, 32 A rows and 64 B rows, and each line is requested
   // about once per XCD.  The loads land in the scratch slot, never read.
   constexpr int PF_DIST = 3;
-  constexpr int PF = (GROUPED || BM != 256) ? 0 : PF_DIST;
+  constexpr int PF = (GROUPED || BM != 256 || NW != 8) ? 0 : PF_DIST;
   const uint8_t* pf_ptr = nullptr;
   if constexpr (PF > 0) {
     const int live = static_cast<int>(row_hi - row_lo);
@@ -446,8 +448,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       dma16(b_base + kof + static_cast<int64_t>(d - A_DMA) * 8 * p.K, voff, lds_tb + so + (d - A_DMA) * 1024);
     } else {
       const int db = d - A_DMA;
-      dma16_masked(b_base + kof + static_cast<int64_t>(db) * 64 * p.K, voff, lds_tb + so + db * 8 * 1024,
-                   uw + 8 * db < B_GROUPS ? ~0ull : 0ull);
+      dma16_masked(b_base + kof + static_cast<int64_t>(db) * NW * 8 * p.K, voff, lds_tb + so + db * NW * 1024,
+                   uw + NW * db < B_GROUPS ? ~0ull : 0ull);
     }
   };
   auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
@@ -475,7 +477,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) gemm_fp8_block_kernel(FParams p) 
       if (!((a_live[i] >> lane) & 1)) {
 #pragma unroll
         for (int s0 = 0; s0 < STAGES; ++s0)
-          *reinterpret_cast<u32x4*>(tiles + s0 * STAGE + (wave * (BM / 8) + i * 8) * 128 + lane * 16) =
+          *reinterpret_cast<u32x4*>(tiles + s0 * STAGE + (wave * (BM / NW) + i * 8) * 128 + lane * 16) =
               u32x4{0u, 0u, 0u, 0u};
       }
     }
@@ -729,7 +731,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(MT * p.NT);
   hipLaunchKernelGGL(
       (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER, SCALED>),
-      dim3(blocks), dim3(NTHREADS), 0, s, p);
+      dim3(blocks), dim3(C::WM * C::WN * 64), 0, s, p);
   return hipGetLastError();
 }
 
