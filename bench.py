@@ -11,10 +11,10 @@ events on its stream, and the quantisers are timed afterwards as batches.  The t
 inputs are rotated over three HBM copies so that the 256 MB last-level cache
 cannot serve the quantisers' reads from one step to the next.
 
-Other workloads (``--workload quant|moe|wgrad|dgrad|pow2``) measure the remaining rows of
+Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused``) measure the remaining rows of
 the path and print their own JSON line; the default run prints exactly one line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2|fused]
                     [--no-cpu-baseline]
 """
 
@@ -279,6 +279,74 @@ def bench_pow2(args, torch, fp8, workloads):
             "fp8_quant_act_1x128_pow2": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
             "fp8_quant_weight_128x128_pow2": _hbm_line("w", t_w.mean_ms() / args.steps, w_bytes, {}),
             "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
+        },
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None},
+    }
+
+
+def bench_fused(args, torch, fp8, workloads):
+    """The dense step with the output cast fused into the GEMM: quantise X and W,
+    then one GEMM that writes Y as E4M3 codes + 1x128 scales (the next layer's
+    input).  The same work unfused -- fp32 Y to HBM, then the 1x128 quantiser --
+    is timed afterwards; both give the same bytes."""
+    M, N, K = 4096, 7168, 7168
+    d = workloads.dense()
+    xs = [d["x"].cuda() for _ in range(3)]
+    ws = [d["w"].cuda() for _ in range(3)]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    qy = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    sy = torch.empty((M, N // 128), dtype=torch.float32, device="cuda")
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    t_f, t_g, t_q = Timer(torch, args.steps), Timer(torch, args.steps), Timer(torch, args.steps)
+
+    def step(i, timed):
+        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
+        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+        if timed:
+            with t_f:
+                fp8.fp8_block_gemm_quant(qa, sa, qb, sb, q=qy, scales=sy)
+        else:
+            fp8.fp8_block_gemm_quant(qa, sa, qb, sb, q=qy, scales=sy)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    # unfused: the same step with fp32 Y written, then quantised by the 1x128 quantiser
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
+        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+        with t_g:
+            fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y32)
+        with t_q:
+            fp8.fp8_quant_act_1x128(y32, qy, sy)
+    torch.cuda.synchronize()
+    dt_unfused = (time.perf_counter() - t1) / args.steps
+    flop = 2.0 * M * N * K
+    fms = t_f.mean_ms()
+    tf = flop / (fms * 1e-3) / 1e12
+    return {
+        "metric": "FP8 block-scaled GEMM TFLOP/s, output cast to E4M3 1x128 in the epilogue", "value": flop / dt / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "dense projection with the output quantised for the next layer: quantise X bf16 "
+                               "[4096,7168] 1x128 and W bf16 [7168,7168] 128x128, GEMM Y = X W^T whose epilogue "
+                               "writes Y as E4M3 codes [4096,7168] + fp32 scales [4096,56]",
+                   "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": 3},
+        "kernels": {
+            "fp8_block_gemm_quant": {"ms": fms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
+            "unfused: fp8_block_gemm (fp32 out)": {"ms": t_g.mean_ms()},
+            "unfused: fp8_quant_act_1x128 of Y (fp32)": {"ms": t_q.mean_ms()},
+            "unfused step (ms)": {"ms": dt_unfused * 1e3},
         },
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_FP8_TFLOPS, "traffic": None},
@@ -566,7 +634,7 @@ def main():
     # The first ~100 dense GEMMs of a process run up to 25% slower while the
     # clocks ramp up; the default warm-up covers that ramp.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -587,7 +655,8 @@ def main():
     from fp8_fine_grained_amd import workloads
 
     fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
-          "dgrad": bench_dgrad, "pow2": bench_pow2}[args.workload]
+          "dgrad": bench_dgrad, "pow2": bench_pow2,
+          "fused": bench_fused}[args.workload]
     out = fn(args, torch, fp8, workloads)
     print(json.dumps(out), flush=True)
 

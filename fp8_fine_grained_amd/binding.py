@@ -38,6 +38,8 @@ _SIGS = {
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                        _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
+    "fp8_block_gemm_quant": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                             _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8_block_grouped_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
                                _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64,
                                _c.c_int64, _c.c_int64, _c.c_void_p],
@@ -200,6 +202,24 @@ def fp8_block_gemm(a, sa, b, sb, b_scale_mode="block", accum=None, out_dtype=tor
                               _ptr(y), _dtype_code(y.dtype), M, N, K, _stream(stream))
     _check("fp8_block_gemm", st)
     return y
+
+
+def fp8_block_gemm_quant(a, sa, b, sb, accum="fp8", pow2=False, q=None, scales=None, stream=None):
+    """Y = deq(a) deq(b)^T leaving the GEMM 1x128-quantised: returns (q uint8 [M, N],
+    scales fp32 [M, N/128]); ``accum`` "fp8" or "scaled", ``pow2`` power-of-two scales."""
+    _on_gpu(a, sa, b, sb)
+    M, K = a.shape
+    N = b.shape[0]
+    if q is None:
+        q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    if scales is None:
+        scales = torch.empty((M, N // 128), dtype=torch.float32, device=a.device)
+    _on_gpu(q, scales)
+    _contig(a, sa, b, sb, q, scales)
+    st = lib().fp8_block_gemm_quant(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _accum_code(accum, torch.bfloat16),
+                                    1 if pow2 else 0, _ptr(q), _ptr(scales), M, N, K, _stream(stream))
+    _check("fp8_block_gemm_quant", st)
+    return q, scales
 
 
 def fp8_block_grouped_gemm(a, sa, offsets, b, sb, accum=None, out_dtype=torch.bfloat16, y=None,

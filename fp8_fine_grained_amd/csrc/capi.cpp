@@ -166,6 +166,25 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const fl
   return hip_status(fp8fg::launch_block_gemm(g, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_block_gemm_quant(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int accum,
+                         int pow2, uint8_t* q_y, float* s_y, int64_t M, int64_t N, int64_t K,
+                         fp8fg_stream_t stream) {
+  if (accum == FP8FG_ACCUM_EXACT || (pow2 != 0 && pow2 != 1)) return accum == FP8FG_ACCUM_EXACT
+                                                                        ? FP8FG_ERR_UNSUPPORTED
+                                                                        : FP8FG_ERR_INVALID_ARG;
+  const int c = check_gemm_common(a, sa, b, sb, accum, q_y, FP8FG_BF16, M, N, K);
+  if (c < 0) return FP8FG_OK;
+  if (c != FP8FG_OK) return c;
+  if (!s_y) return FP8FG_ERR_INVALID_ARG;
+  if (!aligned(s_y, 4)) return FP8FG_ERR_MISALIGNED;
+  if (N % 256 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (((M + 127) / 128) * (N / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  fp8fg::GemmArgs g = gemm_args(a, sa, b, sb, q_y, nullptr, M, N, K, 1, false, accum, FP8FG_BF16);
+  g.y_scales = s_y;
+  if (!fp8fg::fp8_block_kernel_applies(g)) return FP8FG_ERR_UNSUPPORTED;
+  return hip_status(fp8fg::launch_fp8_block_gemm_quant(g, pow2 == 1, static_cast<hipStream_t>(stream)));
+}
+
 int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* group_offsets,
                            int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
                            int y_dtype, int64_t M_total, int64_t N, int64_t K,

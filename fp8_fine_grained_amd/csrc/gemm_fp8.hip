@@ -48,6 +48,7 @@
 //    grouped tiles are in expert-major order, so one XCD works through one
 //    expert's tiles at a time.
 #include "launch.h"
+#include "quant_rule.h"
 
 namespace fp8fg {
 namespace {
@@ -74,6 +75,7 @@ struct FParams {
   int KB;  // K / 128
   int MT;  // m-tiles (dense: ceil(M/BM); grouped: upper bound M/BM + G)
   int NT;  // N / BN
+  float* ys;  // quantised output: 1x128 scales [M, N/128] (y holds the E4M3 codes [M, N])
 };
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -184,8 +186,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // GATHER (grouped only): A rows and their scales are read through p.rows.
 // SCALED: power-of-two scales applied by the matrix cores (E8M0 operands of the
 // scaled MFMA), which also accumulate: no separate promotion step.
+// QOUT: the output leaves quantised, 1x128 along N, by the quantisers' rule
+// applied to the fp32 accumulators (1: scale amax/448, 2: power-of-two scale).
 template <int BM, int BN, int WM, int WN, int STAGES, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED,
-          bool GATHER = false, bool SCALED = false>
+          bool GATHER = false, bool SCALED = false, int QOUT = 0>
 __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams p) {
   constexpr int NW = WM * WN;  // wavefronts: 8 (2 per SIMD) or 4 (1 per SIMD)
   static_assert(NW == 8 || NW == 4, "8 or 4 wavefronts");
@@ -218,6 +222,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   static_assert(!(ROWS && GROUPED), "grouped weights carry block scales");
   static_assert(!GATHER || GROUPED, "gathering is a grouped-GEMM mode");
   static_assert(!SCALED || (!EXACT && !ROWS), "the scaled mode takes FP8 products and 128x128 weight scales");
+  static_assert(QOUT == 0 || (TN == 128 && BALIGN && !GROUPED), "a wavefront's row of the tile is one 1x128 group");
   // bf16 epilogue: each wavefront stages its TM x TN result (rows of TN*2 bytes
   // padded by 16) in its own slice of the tile buffer.
   constexpr int EPI_PITCH = TN * 2 + 16;
@@ -670,7 +675,44 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
 
   // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
   __syncthreads();  // every wavefront is done with the tile buffers
-  if constexpr (BF16OUT) {
+  if constexpr (QOUT != 0) {
+    // The wavefront's 128 columns of a row are one 1x128 group.  Row m = j*16 +
+    // (lane & 15) of sub-tile column j sits in lanes l, l^16, l^32, l^48, 32
+    // values each: amax over the lane's values, then over those four lanes.
+    // Codes are staged in LDS as 128-byte rows and leave as whole rows.
+    constexpr int QP = 128 + 16;  // staging pitch (bytes)
+    static_assert(NW * TM * QP <= TILES_BYTES, "staging fits the tile buffers");
+    uint8_t* epi = tiles + wave * TM * QP;
+    const int64_t gcol = (n0 + wn * TN) / 128;  // group index along N
+#pragma unroll
+    for (int j = 0; j < SM; ++j) {
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < SN; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[i][j][r]));
+      am = fmaxf(am, __shfl_xor(am, 16));
+      am = fmaxf(am, __shfl_xor(am, 32));
+      float sc, inv;
+      group_scale<QOUT == 2>(am, sc, inv);
+      const int mr = j * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < SN; ++i)
+        *reinterpret_cast<uint32_t*>(epi + mr * QP + i * 16 + 4 * (lane >> 4)) =
+            cvt4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
+      const int64_t m = row_lo + wm * TM + mr;
+      if (lane < 16 && m < row_hi) p.ys[m * (p.N / 128) + gcol] = sc;
+    }
+    // (ds ops of one wavefront complete in order: no barrier needed here)
+#pragma unroll
+    for (int pass = 0; pass < TM / 8; ++pass) {
+      const int mr = pass * 8 + lane / 8;
+      const int64_t m = row_lo + wm * TM + mr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * QP + (lane % 8) * 16);
+      if (m < row_hi)
+        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.y) + m * p.N + n0 + wn * TN + (lane % 8) * 16) = v;
+    }
+  } else if constexpr (BF16OUT) {
     // Stage the wavefront's TM x TN block as bf16 rows in LDS (8 bytes per lane
     // and sub-tile), then write whole row segments (TN*2 bytes = 16 lanes x 16 B).
     uint8_t* epi = tiles + wave * TM * EPI_PITCH;
@@ -722,15 +764,16 @@ template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN 
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
 template <> struct Cfg<2> { static constexpr int BM = 256, BN = 224, WM = 4, WN = 2, ST = 2; };
 
-template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED>
+template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED, int QOUT = 0>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using C = Cfg<CFG>;
   const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
   FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.row_index, g.M, g.N, g.K, g.G, g.T,
-            static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN)};
+            static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN), g.y_scales};
   const unsigned blocks = static_cast<unsigned>(MT * p.NT);
   hipLaunchKernelGGL(
-      (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER, SCALED>),
+      (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER, SCALED,
+                             QOUT>),
       dim3(blocks), dim3(C::WM * C::WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -788,6 +831,16 @@ hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s)
     return narrow ? launch_out<2, false, false, false, false, true>(g, s)
                   : launch_out<0, false, false, false, false, true>(g, s);
   return narrow ? launch_out<2, false, false, false>(g, s) : launch_out<0, false, false, false>(g, s);
+}
+
+// GEMM whose output leaves 1x128-quantised (256 x 256 dense tiles: a
+// wavefront's 128 columns are one group).  FP8 or scaled accumulation.
+hipError_t launch_fp8_block_gemm_quant(const GemmArgs& g, bool pow2, hipStream_t s) {
+  if (g.scaled)
+    return pow2 ? launch_cfg<0, false, false, false, false, false, true, 2>(g, s)
+                : launch_cfg<0, false, false, false, false, false, true, 1>(g, s);
+  return pow2 ? launch_cfg<0, false, false, false, false, false, false, 2>(g, s)
+              : launch_cfg<0, false, false, false, false, false, false, 1>(g, s);
 }
 
 }  // namespace fp8fg

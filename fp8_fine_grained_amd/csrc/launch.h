@@ -35,6 +35,7 @@ struct GemmArgs {
   bool y_bf16;
   const int32_t* row_index = nullptr;  // grouped with gather: row r of A is a[row_index[r]]
   int64_t T = 0;                       // rows of a (and sa) when gathering
+  float* y_scales = nullptr;           // quantised output: scales [M, N/128] (y = codes [M, N])
 };
 hipError_t launch_block_gemm(const GemmArgs& g, hipStream_t s);
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
@@ -44,5 +45,8 @@ hipError_t launch_grouped_gemm_gather(const GemmArgs& g, hipStream_t s);
 // 256x256-tile FP8-accumulation kernel for 128x128 weight scales (gemm_fp8.hip).
 bool fp8_block_kernel_applies(const GemmArgs& g);
 hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s);
+// Dense GEMM writing its output as 1x128-quantised E4M3 codes (g.y) and scales
+// (g.y_scales); requires N % 256 == 0, block-scaled B, FP8 or scaled accumulation.
+hipError_t launch_fp8_block_gemm_quant(const GemmArgs& g, bool pow2, hipStream_t s);
 
 }  // namespace fp8fg

@@ -19,37 +19,18 @@
 // when the mantissa field exceeds 0x600000 (m > 1.75).  x * inv is exact and
 // |x * inv| <= 448.
 #include "launch.h"
+#include "quant_rule.h"
 
 namespace fp8fg {
 namespace {
 
-constexpr float kE4M3Max = 448.0f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <bool POW2 = false>
-__device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
-  if constexpr (!POW2) {
-    s = amax / kE4M3Max;
-    inv = (s == 0.0f) ? 0.0f : 1.0f / s;
-  } else {
-    const uint32_t b = __float_as_uint(amax);
-    int eb = static_cast<int>(b >> 23) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);  // biased exponent of s
-    eb = eb < 1 ? 1 : eb;  // amax below 448 * 2^-126 (outside the contract): the smallest normal scale
-    s = amax == 0.0f ? 0.0f : __uint_as_float(static_cast<uint32_t>(eb) << 23);
-    inv = amax == 0.0f ? 0.0f : __uint_as_float(static_cast<uint32_t>(254 - eb) << 23);
-  }
-}
 
-// Four fp32 values -> four E4M3 bytes (little-endian order a, b, c, d).
-__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
-  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
-  return static_cast<uint32_t>(v);
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }

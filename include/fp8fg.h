@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 4
+#define FP8FG_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum {
@@ -192,6 +192,26 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
 int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                    int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
                    int64_t K, fp8fg_stream_t stream);
+
+/*
+ * The same GEMM with its output cast straight to FP8 for the next layer: the
+ * "cast fused" into the producer that the tonho.wtf "DeepSeek-V3" page lists
+ * among its hardware wishes ("o que isso custou").  The fp32 accumulators
+ * acc[m, n] (as fp8_block_gemm with FP8FG_F32 output would return them) are
+ * quantised 1x128 along N by the rule of fp8_quant_act_1x128 (pow2 == 0) or of
+ * fp8_quant_act_1x128_pow2 (pow2 == 1), inside the GEMM's epilogue, so Y never
+ * goes to HBM in high precision.
+ *
+ * a, sa, b, sb, accum, M, N, K   as fp8_block_gemm with FP8FG_B_BLOCK_128x128;
+ *           accum FP8FG_ACCUM_FP8_MFMA or FP8FG_ACCUM_SCALED_MFMA
+ *           (FP8FG_ACCUM_EXACT: FP8FG_ERR_UNSUPPORTED).
+ * q_y     out, uint8 E4M3 codes [M, N] row-major (16-byte aligned).
+ * s_y     out, fp32 scales [M, N/128] row-major (4-byte aligned).
+ * Requires N % 256 == 0 and K % 128 == 0.  M == 0 is a no-op.
+ */
+int fp8_block_gemm_quant(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int accum,
+                         int pow2, uint8_t* q_y, float* s_y, int64_t M, int64_t N, int64_t K,
+                         fp8fg_stream_t stream);
 
 /*
  * Grouped block-scaled FP8 GEMM over mixture-of-experts row segments (the

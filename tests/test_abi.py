@@ -22,14 +22,14 @@ def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
                           "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual",
-                          "fp8_block_gemm", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
+                          "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
                           "fp8fg_status_string", "fp8fg_abi_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 4
+    assert L.fp8fg_abi_version() == 5
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -130,3 +130,19 @@ def test_grouped_gather_validation(L):
     assert f(*args(T=1 << 20, K=1 << 13)) == fp8.ERR_UNSUPPORTED  # T * K >= 2^32
     assert f(*args(G=0)) == fp8.OK
     assert f(*args(M=0, a=NULL, idx=NULL)) == fp8.OK
+
+
+def test_gemm_quant_validation(L):
+    f = L.fp8_block_gemm_quant
+    ok = dict(a=GOOD, sa=GOOD, b=GOOD, sb=GOOD, accum=fp8.ACCUM_FP8_MFMA, pow2=0, q=GOOD, s=GOOD,
+              M=4, N=256, K=256, stream=NULL)
+    args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
+    assert f(*args(accum=fp8.ACCUM_EXACT)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(accum=7)) == fp8.ERR_INVALID_ARG
+    assert f(*args(pow2=2)) == fp8.ERR_INVALID_ARG
+    assert f(*args(s=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(s=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(q=BAD)) == fp8.ERR_MISALIGNED
+    assert f(*args(N=128)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(K=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(M=0, a=NULL, q=NULL, s=NULL)) == fp8.OK
