@@ -237,7 +237,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave % WM, wn = wave / WM;
+  // Wavefronts w and w + 4 share a SIMD.  Grouped tiles put the m-halves (or
+  // quarters) of the tile on different wavefronts of each SIMD pair, so that a
+  // tile holding only a few rows of an expert segment, whose wavefronts past
+  // the segment end skip their matrix work, still spreads the remaining
+  // MFMAs over the SIMDs.
+  const int wm = GROUPED ? wave / WN : wave % WM, wn = GROUPED ? wave % WN : wave / WM;
 
   // ---- tile selection
   const int T = p.MT * p.NT;
@@ -500,6 +505,24 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   // the per-column promotion factors sa[m,kb] * sb[nb,kb] (block mode) or sa[m,kb]
   // (row mode, where sb[n,kb] is read per n sub-tile); block 0 here, and the
   // loop requests each next block's right after its barrier.
+  // A wavefront whose rows all lie past the end of the segment (or of the
+  // matrix) has no product to form: it only issues its share of the tile loads
+  // and meets the barriers, so the SIMD it shares runs the other wavefront's
+  // MFMAs alone.
+  const bool wave_live = __builtin_amdgcn_readfirstlane(static_cast<int>(row_lo + wm * TM < row_hi)) != 0;
+  if (!wave_live) {
+    int st = 0;
+    for (int kb = 0; kb < KB; ++kb) {
+      const int st_fill = st == 0 ? STAGES - 1 : st - 1;
+      const int kb_fill = clampkb(kb + STAGES - 1);
+#pragma unroll
+      for (int d = 0; d < ND; ++d) dma_tile(d, kb_fill, st_fill);
+      if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
+      prefetch(clampkb(kb + PF));
+      wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
+      st = st == STAGES - 1 ? 0 : st + 1;
+    }
+  } else {
   v8i fm[SM];
   float f[SM];
   v8i fn;
@@ -671,6 +694,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
     promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
   }
+  }  // live wavefront
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
   // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
