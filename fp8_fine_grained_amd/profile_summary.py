@@ -6,6 +6,15 @@ Usage (from the repository root, after copying rocprofv3 output back):
     python -m fp8_fine_grained_amd.profile_summary traffic <fetch.csv> <write.csv> \
         <calib_fetch.csv> <calib_write.csv> <kernel-substring> <kernel-source> <out.md> \
         "<fetch command>" "<write command>" "<calibration commands>"
+    python -m fp8_fine_grained_amd.profile_summary mfma <counters.csv> <kernel-substring> <last-n> \
+        <out.md> "<command>"
+
+``mfma`` reads one counter pass (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE (summed
+over the 8 XCDs, so divided by 8 for one XCD's active cycles),
+SQ_INSTS_VALU_MFMA_MOPS_F8 / _F16, SQ_BUSY_CYCLES, LDS counters) over the kernel's
+last n dispatches and derives the matrix-core utilisation (MFMA-busy SIMD
+cycles over active cycles times the 1024 SIMDs), the average clock (active
+cycles over the dispatch's duration) and the matrix-core flop rate.
 
 ``traffic`` averages the FETCH_SIZE / WRITE_SIZE counters (KiB per dispatch)
 over the dispatches whose name contains the substring, and scales each by what
@@ -153,6 +162,73 @@ def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, substr, kernel_s
         f.write("\n".join(lines) + "\n")
 
 
+SIMDS = 1024        # 256 CUs x 4 SIMDs
+XCDS = 8            # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs (one instance each)
+PEAK_CLOCK_GHZ = 2.4
+
+
+def mfma(csv_path, substr, last_n, out_md, command):
+    last_n = int(last_n)
+    per = {}  # dispatch -> {counter: value}, plus timestamps
+    name = None
+    for r in _rows(csv_path):
+        if substr not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"]
+        d = per.setdefault(int(r["Dispatch_Id"]), {"_t": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no dispatches matching {substr!r} in {csv_path}")
+    ds = [per[k] for k in sorted(per)][-last_n:]
+    avg = {k: sum(d.get(k, 0.0) for d in ds) / len(ds) for k in ds[0]}
+    t_s = avg["_t"] * 1e-9
+    active = avg["GRBM_GUI_ACTIVE"] / XCDS  # cycles of one XCD (all run the whole dispatch)
+    util = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * SIMDS)
+    clock = active / t_s / 1e9
+    flops8 = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512
+    flops16 = avg.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512
+    lines = [
+        "# Matrix-core utilisation (rocprofv3 counters)",
+        "",
+        f"Kernel: `{name[:160]}`",
+        "",
+        "Command (repository root on the GPU box):",
+        "",
+        "```",
+        command,
+        "```",
+        "",
+        f"Averages over the kernel's last {len(ds)} dispatches (counters summed over all XCDs and shader engines):",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| dispatch duration (counter run) | {t_s * 1e6:.1f} us |",
+    ]
+    for k in sorted(avg):
+        if k != "_t":
+            lines.append(f"| {k} | {avg[k]:.4g} |")
+    lines += [
+        f"| MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {XCDS} XCDs x {SIMDS} SIMDs) | {util:.3f} |",
+        f"| average clock = (GRBM_GUI_ACTIVE / {XCDS}) / duration | {clock:.2f} GHz |",
+        f"| utilisation x clock / {PEAK_CLOCK_GHZ} GHz (fraction of the published peak's matrix-core cycles) | "
+        f"{util * clock / PEAK_CLOCK_GHZ:.3f} |",
+    ]
+    if "SQ_WAVE_CYCLES" in avg:
+        wc = avg["SQ_WAVE_CYCLES"]
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM"):
+            if k in avg:
+                lines.append(f"| {k} / SQ_WAVE_CYCLES | {avg[k] / wc:.3f} |")
+        lines.append(f"| resident wavefronts per SIMD = 4 x SQ_WAVE_CYCLES / (active cycles x {SIMDS}) | "
+                     f"{4 * wc / (active * SIMDS):.2f} |")
+    if flops8:
+        lines.append(f"| FP8 matrix-core work = MOPS_F8 x 512 | {flops8 / 1e9:.1f} GFLOP, {flops8 / t_s / 1e12:.0f} TFLOP/s |")
+    if flops16:
+        lines.append(f"| F16 matrix-core work = MOPS_F16 x 512 | {flops16 / 1e9:.1f} GFLOP, {flops16 / t_s / 1e12:.0f} TFLOP/s |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def load_traffic(md_path):
     """The JSON record embedded in a traffic summary (None if absent)."""
     try:
@@ -174,5 +250,7 @@ if __name__ == "__main__":
         stats(*sys.argv[2:6])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:12])
+    elif sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:7])
     else:
         raise SystemExit(__doc__)
