@@ -52,6 +52,21 @@ def _traffic(record_name, kernel_src):
     return rec.get("per_launch_bytes")
 
 
+def _mfma_counters(record_name):
+    """Matrix-core utilisation of the GEMM from a committed rocprofv3 counter
+    summary (MFMA-busy fraction of the active cycles, the average clock, and
+    their product over the 2.4 GHz of the published peak), or None when the
+    GEMM source has changed since the counters were taken."""
+    from fp8_fine_grained_amd.profile_summary import load_traffic
+
+    src = os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip")
+    rec = load_traffic(os.path.join(ROOT, "profiles", record_name))
+    if not rec or rec.get("kernel_source_sha256") != _sha(src):
+        return None
+    return {"mfma_busy_fraction": rec["mfma_busy_fraction"], "clock_ghz": rec["clock_ghz"],
+            "fraction_of_peak_mfma_cycles": rec["fraction_of_peak_mfma_cycles"], "source": "profiles/" + record_name}
+
+
 class Timer:
     """HIP-event timing of one kernel launch site on the stream it is launched on.
 
@@ -216,6 +231,7 @@ def bench_dense(args, torch, fp8, workloads):
             "unit": "TFLOP/s",
             "frac": gemm_tflops / PEAK_FP8_TFLOPS,
             "traffic": traffic,
+            "mfma_counters": _mfma_counters("block_gemm_dense_4096x7168x7168_mfma_util.md"),
         },
     }
     if not args.no_cpu_baseline:
@@ -281,7 +297,8 @@ def bench_pow2(args, torch, fp8, workloads):
             "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
         },
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None},
+                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None,
+                     "mfma_counters": _mfma_counters("block_gemm_pow2_4096x7168x7168_mfma_util.md")},
     }
 
 
@@ -498,7 +515,8 @@ def bench_moe(args, torch, fp8, workloads):
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": _traffic("grouped_gemm_moe_65536x2048x7168_traffic.md",
-                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip"))},
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip")),
+                     "mfma_counters": _mfma_counters("grouped_gemm_moe_65536x2048x7168_mfma_util.md")},
     }
 
 
@@ -548,7 +566,8 @@ def bench_wgrad(args, torch, fp8, workloads):
                                                        "frac_fp8_peak": flop / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
         },
         "roofline": {"bound": "mfma", "achieved": flop / (gms * 1e-3) / 1e12, "peak": PEAK_FP16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, "traffic": None,
+                     "mfma_counters": _mfma_counters("wgrad_exact_7168x7168x16384_mfma_util.md")},
     }
 
 

@@ -7,7 +7,7 @@ Usage (from the repository root, after copying rocprofv3 output back):
         <calib_fetch.csv> <calib_write.csv> <kernel-substring> <kernel-source> <out.md> \
         "<fetch command>" "<write command>" "<calibration commands>"
     python -m fp8_fine_grained_amd.profile_summary mfma <counters.csv> <kernel-substring> <last-n> \
-        <out.md> "<command>"
+        <kernel-source> <out.md> "<command>"
 
 ``mfma`` reads one counter pass (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE (summed
 over the 8 XCDs, so divided by 8 for one XCD's active cycles),
@@ -167,7 +167,7 @@ XCDS = 8            # GRBM_GUI_ACTIVE is reported summed over the 8 XCDs (one in
 PEAK_CLOCK_GHZ = 2.4
 
 
-def mfma(csv_path, substr, last_n, out_md, command):
+def mfma(csv_path, substr, last_n, kernel_src, out_md, command):
     last_n = int(last_n)
     per = {}  # dispatch -> {counter: value}, plus timestamps
     name = None
@@ -225,6 +225,12 @@ def mfma(csv_path, substr, last_n, out_md, command):
         lines.append(f"| FP8 matrix-core work = MOPS_F8 x 512 | {flops8 / 1e9:.1f} GFLOP, {flops8 / t_s / 1e12:.0f} TFLOP/s |")
     if flops16:
         lines.append(f"| F16 matrix-core work = MOPS_F16 x 512 | {flops16 / 1e9:.1f} GFLOP, {flops16 / t_s / 1e12:.0f} TFLOP/s |")
+    with open(kernel_src, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    rec = {"kernel": name[:200], "kernel_source": kernel_src, "kernel_source_sha256": sha,
+           "dispatches_averaged": len(ds), "duration_us": t_s * 1e6, "mfma_busy_fraction": util,
+           "clock_ghz": clock, "fraction_of_peak_mfma_cycles": util * clock / PEAK_CLOCK_GHZ}
+    lines += ["", "```json", json.dumps(rec, indent=1), "```"]
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -251,6 +257,6 @@ if __name__ == "__main__":
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:12])
     elif sys.argv[1] == "mfma":
-        mfma(*sys.argv[2:7])
+        mfma(*sys.argv[2:8])
     else:
         raise SystemExit(__doc__)
