@@ -55,7 +55,7 @@ def stats(csv_path, out_md, command, bench_log=None):
     lines = [
         "# rocprofv3 kernel statistics",
         "",
-        "Command (repository root on the GPU box):",
+        "Command (run from the repository root):",
         "",
         "```",
         command,
@@ -142,7 +142,7 @@ def traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, substr, kernel_s
         "",
         f"Kernel: `{name[:160]}`",
         "",
-        "Commands (repository root on the GPU box, one counter per run):",
+        "Commands (run from the repository root, one counter per run):",
         "",
         "```",
         fetch_cmd,
@@ -192,7 +192,7 @@ def mfma(csv_path, substr, last_n, kernel_src, out_md, command):
         "",
         f"Kernel: `{name[:160]}`",
         "",
-        "Command (repository root on the GPU box):",
+        "Command (run from the repository root):",
         "",
         "```",
         command,
