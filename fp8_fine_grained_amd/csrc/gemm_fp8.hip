@@ -8,9 +8,10 @@
 //
 // Layout on gfx950:
 //  * 512-thread workgroups (8 wavefronts, 2 per SIMD; the template also takes 4,
-//    one per SIMD, which measured 4% slower on the grouped GEMM), each wavefront owning a
-//    (TN x TM) block of 16 x 16 sub-tiles.  Two tile shapes:
+//    one per SIMD), each wavefront owning a (TN x TM) block of 16 x 16
+//    sub-tiles.  Tile shapes:
 //      dense   256 (m) x 256 (n), wavefronts 4 (m) x 2 (n) of 64 x 128, 2 stages;
+//      dense, power-of-two scales: 256 x 256, wavefronts 2 x 2 of 128 x 128;
 //      grouped 128 (m) x 256 (n), wavefronts 2 (m) x 4 (n) of 64 x 64, 3 stages
 //    (128-row tiles waste less of the last tile of each ~256-row expert segment).
 //    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
@@ -212,7 +213,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   constexpr int A_DMA = BM / 8 / NW, B_DMA = (B_GROUPS + NW - 1) / NW;
   constexpr int SA_WAVES = BM / 64;                  // wavefronts loading the A scales (64 rows each)
   constexpr int SB_WAVES = ROWS ? BN / 64 : 1;       // and the B scales (64 rows, or all blocks)
-  static_assert(SA_WAVES + SB_WAVES <= NW, "one scale DMA per wavefront");
+  // With four wavefronts and 256 rows every wavefront loads A scales and
+  // wavefront 0 also the weight-block scales (two scale DMAs; two stages only,
+  // where every wait drains all loads, so the uneven count does not matter).
+  constexpr bool SB_EXTRA = SA_WAVES + SB_WAVES > NW;
+  static_assert(!SB_EXTRA || (SA_WAVES == NW && !ROWS && STAGES == 2), "one scale DMA per wavefront");
   constexpr int SB_LEN = ROWS ? BN : 64;
   constexpr int NB = BALIGN ? BN / 128 : BN / 128 + 2;  // weight blocks a tile can touch (block mode)
   // loads per wavefront per stage: tiles + one scale (or filler) DMA
@@ -417,6 +422,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   const uint32_t lds_s0 = uwave < SA_WAVES ? lds_addr(&s_sa[0][uwave * 64])
                           : (b_scale_wave ? lds_addr(&s_sb[0][(uwave - SA_WAVES) * 64]) : lds_addr(s_filler));
   const uint32_t lds_s_step = uwave < SA_WAVES ? BM * 4 : (b_scale_wave ? SB_LEN * 4 : 0);
+  const float* gsb = nullptr;  // weight-block scales of the extra scale DMA
+  if constexpr (SB_EXTRA) {
+    int64_t blk = n0 / 128 + (lane < NB - 1 ? lane : NB - 1);
+    blk = blk < p.N / 128 ? blk : p.N / 128 - 1;
+    gsb = bscale + blk * p.KB;
+  }
 
   // L2 prefetch (256 x 256 dense tiles): in iteration kb every wavefront touches
   // one dword of K block kb + PF_DIST in 12 rows, so the lines are on their way
@@ -428,11 +439,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   // touches one slice, 32 A rows and 64 B rows, and each line is requested
   // about once per XCD.  The loads land in the scratch slot, never read.
   constexpr int PF_DIST = 3;
-  constexpr int PF = (GROUPED || BM != 256 || NW != 8) ? 0 : PF_DIST;
+  constexpr int PF = (GROUPED || BM != 256) ? 0 : PF_DIST;
   const uint8_t* pf_ptr = nullptr;
   if constexpr (PF > 0) {
     const int live = static_cast<int>(row_hi - row_lo);
-    const int slot = uw * 12 + lane % 12;  // 96 rows over 8 wavefronts
+    const int slot = uw * (96 / NW) + lane % (96 / NW);  // 96 rows over the wavefronts
     if (slot < BM / 8) {
       int r = (nt % 8) * (BM / 8) + slot;
       r = r < live ? r : live - 1;
@@ -462,7 +473,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
                    uw + NW * db < B_GROUPS ? ~0ull : 0ull);
     }
   };
-  auto dma_scale = [&](int kb, int st) { dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step); };
+  auto dma_scale = [&](int kb, int st) {
+    dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step);
+    if constexpr (SB_EXTRA) {
+      if (uwave == 0) dma4(gsb + kb, lds_addr(&s_sb[0][0]) + static_cast<uint32_t>(st) * (SB_LEN * 4));
+    }
+  };
   auto issue = [&](int kb, int st) {
 #pragma unroll
     for (int d = 0; d < ND; ++d) dma_tile(d, kb, st);
@@ -783,10 +799,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
 //   0: 256 x 256, 4 x 2 wavefronts (64 x 128 each), 2 stages (128 KB LDS)
 //   1: 128 x 256, 2 x 4 wavefronts (64 x 64 each), 3 stages (144 KB LDS)
 //   2: 256 x 224, 4 x 2 wavefronts (64 x 112 each), 2 stages (120 KB LDS)
+//   3: 256 x 256, 2 x 2 wavefronts (128 x 128 each, one per SIMD), 2 stages:
+//      scaled mode only, where the 256 accumulators per lane sit in AGPRs and
+//      the matrix cores accumulate into them directly (with fp32 scales the
+//      promotion would have to move every accumulator through VGPRs: 22% slower)
 template <int CFG> struct Cfg;
 template <> struct Cfg<0> { static constexpr int BM = 256, BN = 256, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, ST = 3; };
 template <> struct Cfg<2> { static constexpr int BM = 256, BN = 224, WM = 4, WN = 2, ST = 2; };
+template <> struct Cfg<3> { static constexpr int BM = 256, BN = 256, WM = 2, WN = 2, ST = 2; };
 
 template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED, int QOUT = 0>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
@@ -851,9 +872,12 @@ hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s)
     return g.row_scales ? launch_out<1, true, true, false>(g, s) : launch_out<1, true, false, false>(g, s);
   if (g.row_scales) return launch_out<1, false, true, false>(g, s);
   const bool narrow = dense_tile_width(g) == 224;
+  // (scaled mode: four wavefronts of 128 x 128 on 256 x 256 tiles, 2.5% faster
+  // than eight of 64 x 128 on 4096 x 7168 x 7168: half the fragment reads and
+  // half the wavefronts at each barrier)
   if (g.scaled)
     return narrow ? launch_out<2, false, false, false, false, true>(g, s)
-                  : launch_out<0, false, false, false, false, true>(g, s);
+                  : launch_out<3, false, false, false, false, true>(g, s);
   return narrow ? launch_out<2, false, false, false>(g, s) : launch_out<0, false, false, false>(g, s);
 }
 
@@ -861,8 +885,8 @@ hipError_t launch_fp8_block_gemm(const GemmArgs& g, bool grouped, hipStream_t s)
 // wavefront's 128 columns are one group).  FP8 or scaled accumulation.
 hipError_t launch_fp8_block_gemm_quant(const GemmArgs& g, bool pow2, hipStream_t s) {
   if (g.scaled)
-    return pow2 ? launch_cfg<0, false, false, false, false, false, true, 2>(g, s)
-                : launch_cfg<0, false, false, false, false, false, true, 1>(g, s);
+    return pow2 ? launch_cfg<3, false, false, false, false, false, true, 2>(g, s)
+                : launch_cfg<3, false, false, false, false, false, true, 1>(g, s);
   return pow2 ? launch_cfg<0, false, false, false, false, false, false, 2>(g, s)
               : launch_cfg<0, false, false, false, false, false, false, 1>(g, s);
 }
