@@ -430,14 +430,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   }
 
   // L2 prefetch (256 x 256 dense tiles): in iteration kb every wavefront touches
-  // one dword of K block kb + PF_DIST in 12 rows, so the lines are on their way
+  // one dword of K block kb + PF_DIST in 96 / NW rows, so the lines are on their way
   // from HBM two iterations before the DMAs ask for them (the DMAs' own lead is
   // one iteration, which covers the latency of the last-level cache but not that
   // of HBM, e.g. right after the quantisers have written the operands).  The
   // tiles that run at the same time on one XCD share their panels (with the
   // band order: 8 n-tiles per A panel, 4 m-tiles per B panel), so each tile
   // touches one slice, 32 A rows and 64 B rows, and each line is requested
-  // about once per XCD.  The loads land in the scratch slot, never read.
+  // about once per XCD.  The loads land in the LDS filler slot, never read.
   constexpr int PF_DIST = 3;
   constexpr int PF = (GROUPED || BM != 256) ? 0 : PF_DIST;
   const uint8_t* pf_ptr = nullptr;

@@ -121,6 +121,14 @@ def test_act_cols_small():
     _act_cols(torch.from_numpy(_special_tiles().T.copy()), "special fp32")
 
 
+def test_act_cols_xcd_ordered_grid():
+    # 8 token groups x 2 or 3 column blocks: block counts divisible by 8 take the
+    # XCD-contiguous block order (the other tests' small grids do not)
+    d = workloads.wgrad(T=1024, C=256, Cin=384)
+    _act_cols(d["dy"], "dY 16 blocks")
+    _act_cols(d["x"], "X 24 blocks")
+
+
 def test_weight_small():
     for w, what in ((workloads.tiny()["w"], "tiny fp32"),
                     (workloads.dense(M=1, N=384, K=1024)["w"], "dense-like bf16"),
