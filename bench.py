@@ -297,7 +297,9 @@ def bench_pow2(args, torch, fp8, workloads):
             "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
         },
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None,
+                     "frac": tf / PEAK_FP8_TFLOPS,
+                     "traffic": _traffic("block_gemm_pow2_4096x7168x7168_traffic.md",
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip")),
                      "mfma_counters": _mfma_counters("block_gemm_pow2_4096x7168x7168_mfma_util.md")},
     }
 
