@@ -48,6 +48,8 @@
 //    contiguous band of the tile grid, keeping its operand panels in its L2;
 //    grouped tiles are in expert-major order, so one XCD works through one
 //    expert's tiles at a time.
+#include <atomic>
+
 #include "launch.h"
 #include "quant_rule.h"
 
@@ -77,7 +79,23 @@ struct FParams {
   int MT;  // m-tiles (dense: ceil(M/BM); grouped: upper bound M/BM + G)
   int NT;  // N / BN
   float* ys;  // quantised output: 1x128 scales [M, N/128] (y holds the E4M3 codes [M, N])
+  // Dense fp32 outputs: tiles 0 .. T_full-1 run whole; each later tile (those
+  // of a partial last round of the CUs) is split into `split` K ranges run by
+  // separate workgroups, which add their fp32 results into the zeroed output.
+  int T_full;
+  int split;
 };
+
+// Dense tile order: bands of GROUP_M m-tiles, n-tile major inside a band, so the
+// tiles an XCD runs together share their A and B panels.
+__device__ __forceinline__ void dense_tile_coords(int t, int MT, int NT, int& mt, int& nt) {
+  const int band = t / (GROUP_M * NT);
+  const int first = band * GROUP_M;
+  const int gsz = (MT - first) < GROUP_M ? (MT - first) : GROUP_M;
+  const int r = t - band * GROUP_M * NT;
+  mt = first + r % gsz;
+  nt = r / gsz;
+}
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -253,6 +271,26 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   const int T = p.MT * p.NT;
   const int bid = blockIdx.x;
   int t = (T % 8 == 0) ? (bid % 8) * (T / 8) + bid / 8 : bid;
+  // K range of this workgroup (in 128-blocks) and whether it adds into the
+  // output: the K-split parts of the tiles past T_full (dense fp32 only) come
+  // after the whole tiles in the grid, and the parts of one tile run on
+  // consecutive workgroups (so on different XCDs).
+  int kb_begin = 0, kb_count = p.KB;
+  bool add_out = false;
+  if constexpr (!GROUPED && !BF16OUT && QOUT == 0) {
+    if (p.split > 1) {
+      if (bid < p.T_full) {
+        t = (p.T_full % 8 == 0) ? (bid % 8) * (p.T_full / 8) + bid / 8 : bid;
+      } else {
+        const int u = bid - p.T_full;
+        const int part = u % p.split;
+        t = p.T_full + u / p.split;
+        kb_begin = static_cast<int>(static_cast<int64_t>(part) * p.KB / p.split);
+        kb_count = static_cast<int>(static_cast<int64_t>(part + 1) * p.KB / p.split) - kb_begin;
+        add_out = true;
+      }
+    }
+  }
   int mt, nt;
   if constexpr (GROUPED) {
     // The grid covers an upper bound of the m-tiles; the live ones are counted
@@ -285,12 +323,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     __syncthreads();  // tile_info is rewritten below
   }
   if constexpr (!GROUPED) {
-    const int band = t / (GROUP_M * p.NT);
-    const int first = band * GROUP_M;
-    const int gsz = (p.MT - first) < GROUP_M ? (p.MT - first) : GROUP_M;
-    const int r = t - band * GROUP_M * p.NT;
-    mt = first + r % gsz;
-    nt = r / gsz;
+    dense_tile_coords(t, p.MT, p.NT, mt, nt);
   } else {
     // Expert-major order: the m-tiles of all experts are concatenated and tile
     // t belongs to m-tile t / NT's expert; that expert's mt_g x NT tiles are
@@ -453,7 +486,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     }
   }
   auto prefetch = [&](int kb) {
-    if constexpr (PF > 0) dma4(pf_ptr + static_cast<int64_t>(kb) * 128, lds_addr(s_filler));
+    if constexpr (PF > 0) dma4(pf_ptr + static_cast<int64_t>(kb_begin + kb) * 128, lds_addr(s_filler));
   };
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
   // sub-tile steps that issue them: six of eight for the dense tiles, three of
@@ -461,7 +494,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   // the row-scaled weight-gradient tiles keep: three is 1-8% slower there)
   constexpr int SPREAD = SN >= 7 ? SN - 2 : (SN >= 4 ? (GROUPED ? SN - 1 : SN / 2) : SN);
   auto dma_tile = [&](int d, int kb, int st) {
-    const int64_t kof = static_cast<int64_t>(kb) * 128;
+    const int64_t kof = static_cast<int64_t>(kb_begin + kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
     if (d < A_DMA) {
       if constexpr (GATHER)
@@ -477,9 +510,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     }
   };
   auto dma_scale = [&](int kb, int st) {
-    dma4(gs + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step);
+    dma4(gs + kb_begin + kb, lds_s0 + static_cast<uint32_t>(st) * lds_s_step);
     if constexpr (SB_EXTRA) {
-      if (uwave == 0) dma4(gsb + kb, lds_addr(&s_sb[0][0]) + static_cast<uint32_t>(st) * (SB_LEN * 4));
+      if (uwave == 0) dma4(gsb + kb_begin + kb, lds_addr(&s_sb[0][0]) + static_cast<uint32_t>(st) * (SB_LEN * 4));
     }
   };
   auto issue = [&](int kb, int st) {
@@ -494,7 +527,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
 #pragma unroll
     for (int j = 0; j < SM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int KB = p.KB;
+  const int KB = kb_count;  // K blocks this workgroup multiplies (from kb_begin)
   auto clampkb = [&](int kb) { return kb < KB ? kb : KB - 1; };
   {
     // Rows past the end of the expert's segment (or of the matrix) are never loaded: their LDS
@@ -810,7 +843,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
 #pragma unroll
       for (int i = 0; i < SN; ++i) {
         const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
-        *reinterpret_cast<v4f*>(static_cast<float*>(p.y) + m * p.N + n) = acc[i][j];
+        float* dst = static_cast<float*>(p.y) + m * p.N + n;
+        if (add_out) {
+          // K-split part: add into the zeroed output (hardware fp32 atomics)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[i][j][r]);
+        } else {
+          *reinterpret_cast<v4f*>(dst) = acc[i][j];
+        }
       }
     }
   }
@@ -830,13 +870,68 @@ template <> struct Cfg<1> { static constexpr int BM = 128, BN = 256, WM = 2, WN 
 template <> struct Cfg<2> { static constexpr int BM = 256, BN = 224, WM = 4, WN = 2, ST = 2; };
 template <> struct Cfg<3> { static constexpr int BM = 256, BN = 256, WM = 2, WN = 2, ST = 2; };
 
+// Zeroes the fp32 output of the K-split tiles (tiles T_full .. T_full +
+// gridDim.x - 1 of the dense order) before their parts add into it.  A kernel,
+// not a memset, so the sequence can be captured in a graph.
+template <int BM, int BN>
+__global__ void __launch_bounds__(256) zero_split_tiles_kernel(float* __restrict__ y, int64_t M, int64_t N, int MT,
+                                                               int NT, int T_full) {
+  int mt, nt;
+  dense_tile_coords(T_full + static_cast<int>(blockIdx.x), MT, NT, mt, nt);
+  const int64_t r0 = static_cast<int64_t>(mt) * BM, c0 = static_cast<int64_t>(nt) * BN;
+  for (int idx = threadIdx.x; idx < BM * (BN / 4); idx += 256) {
+    const int r = idx / (BN / 4), c = idx % (BN / 4);
+    if (r0 + r < M) *reinterpret_cast<v4f*>(y + (r0 + r) * N + c0 + 4 * c) = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 template <int CFG, bool EXACT, bool ROWS, bool BF16OUT, bool GROUPED, bool GATHER, bool SCALED, int QOUT = 0>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   using C = Cfg<CFG>;
   const int64_t MT = GROUPED ? g.M / C::BM + g.G : (g.M + C::BM - 1) / C::BM;
   FParams p{g.a, g.sa, g.b, g.sb, g.y, g.offsets, g.row_index, g.M, g.N, g.K, g.G, g.T,
             static_cast<int>(g.K / 128), static_cast<int>(MT), static_cast<int>(g.N / C::BN), g.y_scales};
-  const unsigned blocks = static_cast<unsigned>(MT * p.NT);
+  const int64_t T = MT * p.NT;
+  p.T_full = static_cast<int>(T);
+  p.split = 1;
+  if constexpr (!GROUPED && !BF16OUT && QOUT == 0) {
+    // fp32 output filling at least one round of the CUs: the tiles of the
+    // partial last round are split along K over the CUs that round would leave
+    // idle (the weight-gradient shape 7168 x 7168 has 1568 tiles of 128 x 256,
+    // 6.125 rounds of 256 CUs; its last 32 tiles run as 8 parts each).  The
+    // parts add in whatever order they finish, so those tiles' last bits can
+    // differ between runs.  Smaller problems are not split, which keeps their
+    // results equal bit for bit to the same sums computed by other tile shapes
+    // (the grouped and the output-quantising kernels).
+    const int ncu = device_cus();
+    if (ncu > 0 && T >= ncu) {
+      const int64_t full = (T / ncu) * ncu, rest = T - full;
+      int64_t parts = rest > 0 ? ncu / rest : 1;
+      parts = parts < p.KB ? parts : p.KB;
+      if (parts >= 2) {
+        p.T_full = static_cast<int>(full);
+        p.split = static_cast<int>(parts);
+        hipLaunchKernelGGL((zero_split_tiles_kernel<C::BM, C::BN>), dim3(static_cast<unsigned>(rest)), dim3(256), 0,
+                           s, static_cast<float*>(g.y), g.M, g.N, p.MT, p.NT, p.T_full);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  const unsigned blocks = static_cast<unsigned>(p.T_full + (T - p.T_full) * p.split);
   hipLaunchKernelGGL(
       (gemm_fp8_block_kernel<C::BM, C::BN, C::WM, C::WN, C::ST, EXACT, ROWS, BF16OUT, GROUPED, GATHER, SCALED,
                              QOUT>),

@@ -188,6 +188,13 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
  * y   out, [M, N] row-major of y_dtype
  * Requires K % 128 == 0 and N % 128 == 0 (M is arbitrary); a, b, y 16-byte
  * aligned; sa, sb 4-byte aligned.  M == 0 is a no-op.
+ * FP8FG_F32 output when the output tiles fill the device's compute units at
+ * least once (e.g. the weight gradient 7168 x 7168): the tiles of the partial
+ * last round are split along K over the compute units that round would leave
+ * idle, and the parts add their fp32 sums into y (zeroed by the library on
+ * `stream` first) with atomic adds.  The accuracy is unchanged, but the order
+ * of those additions, and so the last bits of those tiles, can vary from run
+ * to run.  Smaller problems and bf16 outputs are computed in a fixed order.
  */
 int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                    int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
@@ -197,7 +204,8 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const fl
  * The same GEMM with its output cast straight to FP8 for the next layer: the
  * "cast fused" into the producer that the tonho.wtf "DeepSeek-V3" page lists
  * among its hardware wishes ("o que isso custou").  The fp32 accumulators
- * acc[m, n] (as fp8_block_gemm with FP8FG_F32 output would return them) are
+ * acc[m, n] (as fp8_block_gemm with FP8FG_F32 output returns them, apart from
+ * the run-to-run bit differences of its K-split tiles) are
  * quantised 1x128 along N by the rule of fp8_quant_act_1x128 (pow2 == 0) or of
  * fp8_quant_act_1x128_pow2 (pow2 == 1), inside the GEMM's epilogue, so Y never
  * goes to HBM in high precision.

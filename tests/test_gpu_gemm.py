@@ -61,6 +61,28 @@ def test_dense_shapes_bf16(M, N, K):
     check_f32(_run(g, M, N, torch.float32, "exact"), ref, "exact accum fp32")
 
 
+@pytest.mark.parametrize("K", [256, 1024])
+def test_dense_fp32_k_split_tail(K):
+    # fp32 outputs filling at least one round of the 256 CUs: the tiles of the
+    # partial last round run as K-split parts that add into the zeroed output.
+    # 4352x4096: 272 tiles of 256x256 (FP8 accumulation) and 544 of 128x256
+    # (exact), so 16 and 32 tiles in min(256 / 16 or 32, K / 128) parts.
+    M, N = 4352, 4096
+    d = workloads.dense(M=M, N=N, K=K)
+    g, r = _quantised(d["x"], d["w"])
+    ref = gemm.block_gemm(*r)
+    say(f"dense fp32 {M}x{N}x{K}")
+    check_f32(_run(g, M, N, torch.float32, "exact"), ref, "exact accumulation")
+    y8 = f32(_run(g, M, N, torch.float32, "fp8")).astype(np.float64)
+    # (the per-element FP8 bound needs M x N x 8 temporaries: checked on the
+    # last 256 rows, which hold the split tiles, and the bf16 tolerance elsewhere)
+    rows = slice(M - 256, M)
+    bound = fp8_mfma_bound(r[0][rows], r[1][rows], r[2], r[3], "block")
+    say(f"  fp8 accumulation, last 256 rows: max err/bound {np.max(np.abs(y8[rows] - ref[rows]) / bound):.3f}")
+    assert np.all(np.abs(y8[rows] - ref[rows]) <= bound)
+    check_bf16(y8, ref, "fp8 accumulation (bf16 tolerance)")
+
+
 def test_zero_rows_give_zero():
     d = workloads.dense(M=130, N=256, K=512)
     x = d["x"].clone()
