@@ -445,6 +445,68 @@ def bench_quant(args, torch, fp8, workloads):
     }
 
 
+def bench_tiny(args, torch, fp8, workloads):
+    # The small configuration: X fp32 [128,256] (1% of entries x50), W fp32
+    # [128,256]; quantise both, then the block-scaled GEMM with fp32 output and
+    # exact accumulation.  It is latency-bound (8.4 MFLOP), so the step is timed
+    # as one back-to-back batch inside a single event pair.
+    t = workloads.tiny()
+    x, w = t["x"].cuda(), t["w"].cuda()
+    M, K = x.shape
+    N = w.shape[0]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp8.fp8_quant_act_1x128(x, qa, sa)
+        fp8.fp8_quant_weight_128x128(w, qb, sb)
+        fp8.fp8_block_gemm(qa, sa, qb, sb, accum="exact", y=y)
+
+    tb, tg = Timer(torch, 1), Timer(torch, 1)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with tb:
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    with tg:
+        for _ in range(args.steps):
+            fp8.fp8_block_gemm(qa, sa, qb, sb, accum="exact", y=y)
+    # The same step captured once in a HIP graph and replayed: one submission
+    # for the three kernels instead of three launches.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    tr = Timer(torch, 1)
+    with tr:
+        for _ in range(args.steps):
+            graph.replay()
+    step_ms, gemm_ms, replay_ms = tb.mean_ms() / args.steps, tg.mean_ms() / args.steps, tr.mean_ms() / args.steps
+    flop = 2.0 * M * N * K
+    tf = flop / (gemm_ms * 1e-3) / 1e12
+    return {
+        "metric": "small-case step latency (us)", "value": step_ms * 1e3, "unit": "us", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3, "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "small case: X fp32 [128,256] N(0,1) with 1% x50 outliers, W fp32 [128,256] "
+                               "N(0,0.02); 1x128 and 128x128 quantisation, block-scaled GEMM, fp32 out, exact "
+                               "accumulation", "M": M, "N": N, "K": K},
+        "kernels": {"step (3 launches, event-timed batch)": {"us": step_ms * 1e3},
+                    "step as one HIP graph replay": {"us": replay_ms * 1e3},
+                    "fp8_block_gemm": {"us": gemm_ms * 1e3, "TFLOP/s": tf}},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_FP16_TFLOPS, "traffic": None},
+    }
+
+
 def bench_moe(args, torch, fp8, workloads):
     # One step of the MoE up-projection: quantise the 8192 tokens 1x128, then the
     # grouped GEMM reads each routed row from its token (FP8 dispatch by index).
@@ -655,14 +717,14 @@ def main():
     # The first ~100 dense GEMMs of a process run up to 25% slower while the
     # clocks ramp up; the default warm-up covers that ramp.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): this "
-              "build has no multi-GPU path; run with --gpus 1", file=sys.stderr)
+              "library has no multi-GPU path; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -677,7 +739,7 @@ def main():
 
     fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
           "dgrad": bench_dgrad, "pow2": bench_pow2,
-          "fused": bench_fused}[args.workload]
+          "fused": bench_fused, "tiny": bench_tiny}[args.workload]
     out = fn(args, torch, fp8, workloads)
     print(json.dumps(out), flush=True)
 
