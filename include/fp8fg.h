@@ -192,7 +192,8 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
  * least once (e.g. the weight gradient 7168 x 7168): the tiles of the partial
  * last round are split along K over the compute units that round would leave
  * idle, and the parts add their fp32 sums into y (zeroed by the library on
- * `stream` first) with atomic adds.  The accuracy is unchanged, but the order
+ * `stream` first) with hardware fp32 atomic adds, which need y in ordinary
+ * (coarse-grained) device memory such as hipMalloc or PyTorch returns.  The accuracy is unchanged, but the order
  * of those additions, and so the last bits of those tiles, can vary from run
  * to run.  Smaller problems and bf16 outputs are computed in a fixed order.
  */
