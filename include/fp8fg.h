@@ -193,9 +193,10 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
  * last round are split along K over the compute units that round would leave
  * idle, and the parts add their fp32 sums into y (zeroed by the library on
  * `stream` first) with hardware fp32 atomic adds, which need y in ordinary
- * (coarse-grained) device memory such as hipMalloc or PyTorch returns.  The accuracy is unchanged, but the order
- * of those additions, and so the last bits of those tiles, can vary from run
- * to run.  Smaller problems and bf16 outputs are computed in a fixed order.
+ * (coarse-grained) device memory such as hipMalloc or PyTorch returns.  The
+ * accuracy is unchanged, but the order of those additions, and so the last
+ * bits of those tiles, can vary from run to run.  Smaller problems and bf16
+ * outputs are computed in a fixed order.
  */
 int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
                    int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
