@@ -445,6 +445,75 @@ def bench_quant(args, torch, fp8, workloads):
     }
 
 
+def bench_pertensor(args, torch, fp8, workloads):
+    # The dense projection with ONE scale per tensor (the practice the 1x128 /
+    # 128x128 grouping replaces): per-tensor quantisation of X and W (an amax
+    # pass, then the cast: X and W are read twice), then the same block GEMM,
+    # whose scales are then all equal.  The fine-grained quantisers are timed
+    # on the same inputs beside it.
+    d = workloads.dense()
+    M, K = d["x"].shape
+    N = d["w"].shape[0]
+    xs = [d["x"].cuda() for _ in range(3)]
+    ws = [d["w"].cuda() for _ in range(3)]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    tx, tw, tg = Timer(torch, args.steps), Timer(torch, args.steps), Timer(torch, args.steps)
+
+    def step(i, timed):
+        if timed:
+            with tx:
+                fp8.fp8_quant_per_tensor(xs[i % 3], "act", qa, sa)
+            with tw:
+                fp8.fp8_quant_per_tensor(ws[i % 3], "weight", qb, sb)
+            with tg:
+                fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
+        else:
+            fp8.fp8_quant_per_tensor(xs[i % 3], "act", qa, sa)
+            fp8.fp8_quant_per_tensor(ws[i % 3], "weight", qb, sb)
+            fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    fa, fw = Timer(torch, 1), Timer(torch, 1)
+    with fa:
+        for i in range(args.steps):
+            fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
+    with fw:
+        for i in range(args.steps):
+            fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+    flop = 2.0 * M * N * K
+    gms = tg.mean_ms()
+    tf = flop / (gms * 1e-3) / 1e12
+    return {
+        "metric": "FP8 block GEMM TFLOP/s, per-tensor scales (step incl. per-tensor quantisation)",
+        "value": flop / dt / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": dt * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "dense projection X bf16 [4096,7168] (0.1% x100), W bf16 [7168,7168], one scale per "
+                               "tensor (amax pass + cast), block-scaled FP8 GEMM with uniform scales, bf16 out",
+                   "M": M, "N": N, "K": K, "input_copies_rotated": 3},
+        "kernels": {
+            "fp8_quant_per_tensor (X, 3 launches)": {"ms": tx.mean_ms()},
+            "fp8_quant_per_tensor (W, 3 launches)": {"ms": tw.mean_ms()},
+            "fp8_block_gemm": {"ms": gms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
+            "for comparison: fp8_quant_act_1x128 (X)": {"ms": fa.mean_ms() / args.steps},
+            "for comparison: fp8_quant_weight_128x128 (W)": {"ms": fw.mean_ms() / args.steps},
+        },
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_FP8_TFLOPS, "traffic": None},
+    }
+
+
 def bench_tiny(args, torch, fp8, workloads):
     # The small configuration: X fp32 [128,256] (1% of entries x50), W fp32
     # [128,256]; quantise both, then the block-scaled GEMM with fp32 output and
@@ -717,7 +786,7 @@ def main():
     # The first ~100 dense GEMMs of a process run up to 25% slower while the
     # clocks ramp up; the default warm-up covers that ramp.
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused", "tiny"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused", "tiny", "pertensor"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -739,7 +808,7 @@ def main():
 
     fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
           "dgrad": bench_dgrad, "pow2": bench_pow2,
-          "fused": bench_fused, "tiny": bench_tiny}[args.workload]
+          "fused": bench_fused, "tiny": bench_tiny, "pertensor": bench_pertensor}[args.workload]
     out = fn(args, torch, fp8, workloads)
     print(json.dumps(out), flush=True)
 

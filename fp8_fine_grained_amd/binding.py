@@ -34,6 +34,8 @@ _SIGS = {
                                  _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_quant_weight_128x128_pow2": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    "fp8_quant_per_tensor": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p,
+                             _c.c_void_p, _c.c_int, _c.c_void_p],
     "fp8_quant_weight_128x128_dual": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
@@ -149,6 +151,29 @@ def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None, pow2=False):
     st = getattr(lib(), fn)(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(q),
                             _ptr(scales), _stream(stream))
     _check(fn, st)
+    return q, scales
+
+
+def fp8_quant_per_tensor(x, layout="act", q=None, scales=None, stream=None):
+    """One scale for the whole row-contiguous ``x`` [M, K] (fp8_quant_per_tensor).
+
+    ``layout="act"`` fills scales [M, K/128] (the GEMM's A operand), ``"weight"``
+    scales [M/128, K/128] (its B operand in block mode); every entry is the one
+    scale.  Returns ``(q uint8 [M, K], scales)``."""
+    _on_gpu(x)
+    M, K = x.shape
+    if x.stride(1) != 1:
+        raise ValueError("x must be row-contiguous")
+    mode = {"act": B_ROW_1x128, "weight": B_BLOCK_128x128}[layout]
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        rows = M if layout == "act" else M // 128
+        scales = torch.empty((rows, K // 128), dtype=torch.float32, device=x.device)
+    _on_gpu(q, scales)
+    st = lib().fp8_quant_per_tensor(_ptr(x), _dtype_code(x.dtype), M, K, x.stride(0), _ptr(q), _ptr(scales), mode,
+                                    _stream(stream))
+    _check("fp8_quant_per_tensor", st)
     return q, scales
 
 

@@ -103,6 +103,23 @@ int fp8_quant_weight_128x128_pow2(const void* w, int w_dtype, int64_t N, int64_t
   return quant_weight(w, w_dtype, N, K, ld_w, q, scales, stream, true);
 }
 
+int fp8_quant_per_tensor(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                         float* scales, int scale_layout, fp8fg_stream_t stream) {
+  if (!valid_dtype(x_dtype) || M < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (scale_layout != FP8FG_B_ROW_1x128 && scale_layout != FP8FG_B_BLOCK_128x128) return FP8FG_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return FP8FG_OK;
+  if (K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (scale_layout == FP8FG_B_BLOCK_128x128 && M % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!x || !q || !scales) return FP8FG_ERR_INVALID_ARG;
+  if (ld < K) return FP8FG_ERR_INVALID_ARG;
+  if (M > kInt32Max || K > kInt32Max || M * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || (ld * elem_size(x_dtype)) % 16 != 0)
+    return FP8FG_ERR_MISALIGNED;
+  const int64_t n_scales = (scale_layout == FP8FG_B_ROW_1x128 ? M : M / 128) * (K / 128);
+  return hip_status(fp8fg::launch_quant_per_tensor(x, x_dtype == FP8FG_BF16, M, K, ld, q, scales, n_scales,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                                   uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
                                   fp8fg_stream_t stream) {

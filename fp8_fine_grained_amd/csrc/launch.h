@@ -14,6 +14,10 @@ hipError_t launch_quant_act_rows(const void* x, bool bf16, bool pow2, int64_t M,
 // x is physically [K, ld] row-major, element (m, k) at k*ld + m.
 hipError_t launch_quant_act_cols(const void* x, bool bf16, bool pow2, int64_t M, int64_t K, int64_t ld,
                                  uint8_t* q, float* scales, hipStream_t s);
+// One scale for the whole row-contiguous [M, K] tensor, written into all
+// n_scales entries of `scales` (M * K/128 or (M/128) * (K/128) of them).
+hipError_t launch_quant_per_tensor(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                                   float* scales, int64_t n_scales, hipStream_t s);
 // 128x128 quantisation.
 hipError_t launch_quant_weight(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, int64_t ld,
                                uint8_t* q, float* scales, hipStream_t s);

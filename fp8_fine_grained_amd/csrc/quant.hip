@@ -117,6 +117,81 @@ __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restr
   }
 }
 
+// ---------------------------------------------------------------- per tensor
+// One scale for the whole tensor, the practice the 1x128 / 128x128 grouping
+// replaces (innerforce notes, Figure 7(a) passage), kept for the accuracy and
+// cost comparison: the same rule with the amax taken over every element.
+// Three launches and no workspace: (1) each block's amax into scales[b],
+// (2) one block reduces them and stores s in scales[0], (3) the cast, which
+// reads s from scales[0] and writes it into every other scale slot.
+
+// (1) Blocks stride over 32-tile groups of the row-major [M, K/128] tile grid.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_pt_amax_kernel(const void* __restrict__ x, int64_t ld, int G,
+                                                            int64_t tiles, float* __restrict__ partial) {
+  __shared__ float wave_max[4];
+  const int part = threadIdx.x & 7;
+  constexpr int ES = BF16 ? 2 : 4;
+  float amax = 0.0f;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 32; base < tiles;
+       base += static_cast<int64_t>(gridDim.x) * 32) {
+    const int64_t tile = base + (threadIdx.x >> 3);
+    if (tile < tiles) {
+      const int64_t m = tile / G;
+      const int64_t col = (tile - m * G) * 128 + part * 16;
+      float v[16];
+      load16<BF16>(static_cast<const char*>(x) + (m * ld + col) * ES, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    }
+  }
+  amax = max64(amax);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    partial[blockIdx.x] = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+}
+
+// (2) One block: the amax of the n partial maxima, then s.
+__global__ void __launch_bounds__(256) quant_pt_scale_kernel(float* __restrict__ scales, int n) {
+  __shared__ float wave_max[4];
+  float amax = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) amax = fmaxf(amax, scales[i]);
+  amax = max64(amax);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();  // every partial has been read before scales[0] is overwritten
+  if (threadIdx.x == 0) {
+    float s, inv;
+    group_scale(fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3])), s, inv);
+    scales[0] = s;
+  }
+}
+
+// (3) The cast, laid out as the 1x128 row kernel; tile t also writes scale slot
+// t (t in [1, n_scales)); slot 0 already holds s and is only read.
+template <bool BF16>
+__global__ void __launch_bounds__(256) quant_pt_cast_kernel(const void* __restrict__ x, int64_t ld, int G,
+                                                            int64_t tiles, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scales, int64_t n_scales, int64_t K) {
+  const int64_t tile = static_cast<int64_t>(blockIdx.x) * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  if (tile >= tiles) return;  // no cross-lane operations below
+  const int64_t m = tile / G;
+  const int64_t col = (tile - m * G) * 128 + part * 16;
+  constexpr int ES = BF16 ? 2 : 4;
+  const float s = scales[0];
+  const float inv = (s == 0.0f) ? 0.0f : 1.0f / s;  // as group_scale derives it from the same s
+  float v[16];
+  load16<BF16>(static_cast<const char*>(x) + (m * ld + col) * ES, v);
+  u32x4 out;
+  out.x = cvt4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+  out.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+  out.z = cvt4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
+  out.w = cvt4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
+  __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(q + m * K + col));
+  if (part == 0 && tile >= 1 && tile < n_scales) scales[tile] = s;
+}
+
 // ------------------------------------------------------- 1x128, transposed
 // Input physically [K, ld] (e.g. tokens x channels); logical row m is column m,
 // and a group is 128 consecutive physical rows (tokens) of one column.
@@ -394,6 +469,34 @@ hipError_t launch_quant_act_rows(const void* x, bool bf16, bool pow2, int64_t M,
     pow2 ? go(quant_act_rows_kernel<true, true>) : go(quant_act_rows_kernel<true, false>);
   else
     pow2 ? go(quant_act_rows_kernel<false, true>) : go(quant_act_rows_kernel<false, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_per_tensor(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                                   float* scales, int64_t n_scales, hipStream_t s) {
+  const int G = static_cast<int>(K / 128);
+  const int64_t tiles = M * G;
+  // (1) writes one partial per block into the scale slots, so at most n_scales
+  // blocks (and at most 2048: each then strides over the tile grid)
+  int64_t nb = (tiles + 31) / 32;
+  nb = nb < n_scales ? nb : n_scales;
+  nb = nb < 2048 ? nb : 2048;
+  if (bf16)
+    hipLaunchKernelGGL(quant_pt_amax_kernel<true>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, x, ld, G, tiles,
+                       scales);
+  else
+    hipLaunchKernelGGL(quant_pt_amax_kernel<false>, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, x, ld, G, tiles,
+                       scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quant_pt_scale_kernel, dim3(1), dim3(256), 0, s, scales, static_cast<int>(nb));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(static_cast<unsigned>((tiles + 31) / 32));
+  if (bf16)
+    hipLaunchKernelGGL(quant_pt_cast_kernel<true>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, n_scales, K);
+  else
+    hipLaunchKernelGGL(quant_pt_cast_kernel<false>, grid, dim3(256), 0, s, x, ld, G, tiles, q, scales, n_scales, K);
   return hipGetLastError();
 }
 

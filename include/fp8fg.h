@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 5
+#define FP8FG_ABI_VERSION 6
 
 /* Status codes returned by every entry point. */
 enum {
@@ -134,6 +134,31 @@ int fp8_quant_act_1x128(const void* x, int x_dtype, int64_t M, int64_t K, int64_
  */
 int fp8_quant_act_1x128_pow2(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m,
                              int64_t stride_k, uint8_t* q, float* scales, fp8fg_stream_t stream);
+
+/*
+ * Per-tensor quantisation: ONE scale for the whole tensor, the practice the
+ * 1x128 / 128x128 grouping replaces (innerforce notes, Figure 7(a) passage),
+ * for measuring what the fine-grained grouping buys.  The rule is the
+ * fine-grained one with the group being the whole tensor:
+ *     s = fl32(amax_all / 448), inv = s ? fl32(1/s) : 0, q = E4M3_RNE(fl32(x * inv)).
+ * The scale is written into every entry of a scale array of the layout the
+ * GEMM takes, so the codes and scales feed fp8_block_gemm unchanged.
+ *
+ * x             [M, K] of `x_dtype`, row-contiguous with row pitch ld >= K.
+ * q             out, uint8 E4M3 codes [M, K] row-major.
+ * scales        out, fp32, every entry = s:
+ *                 scale_layout FP8FG_B_ROW_1x128:    [M, K/128]  (activation / A layout)
+ *                 scale_layout FP8FG_B_BLOCK_128x128: [M/128, K/128] (weight / B layout;
+ *                                                      requires M % 128 == 0)
+ *               The array also serves as the kernels' scratch between their
+ *               launches (per-block maxima); its contents are final when the
+ *               stream reaches the end of the call.
+ * Three kernels are enqueued (block maxima, their maximum, the cast), so x is
+ * read twice.  Requires K % 128 == 0; x 16-byte aligned with ld * sizeof(elem)
+ * % 16 == 0; q 16-byte aligned; scales 4-byte aligned.  M == 0 is a no-op.
+ */
+int fp8_quant_per_tensor(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ld, uint8_t* q,
+                         float* scales, int scale_layout, fp8fg_stream_t stream);
 
 /*
  * 128x128 weight quantisation (same passages).

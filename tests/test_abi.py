@@ -21,7 +21,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
-                          "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual",
+                          "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual", "fp8_quant_per_tensor",
                           "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
                           "fp8fg_status_string", "fp8fg_abi_version"}
     for n in names:
@@ -29,7 +29,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 5
+    assert L.fp8fg_abi_version() == 6
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -59,6 +59,24 @@ def test_quant_weight_validation(L, fn):
     assert f(GOOD, fp8.F32, 128, 128, 128, NULL, GOOD, NULL) == fp8.ERR_INVALID_ARG
     assert f(GOOD, fp8.F32, 128, 128, 128, GOOD, ctypes.c_void_p(0x10002), NULL) == fp8.ERR_MISALIGNED
     assert f(NULL, fp8.F32, 0, 128, 128, NULL, NULL, NULL) == fp8.OK
+
+
+def test_quant_per_tensor_validation(L):
+    f = L.fp8_quant_per_tensor
+    ok = dict(x=GOOD, dt=fp8.BF16, M=128, K=256, ld=256, q=GOOD, s=GOOD, layout=fp8.B_ROW_1x128, stream=NULL)
+    args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
+    assert f(*args(x=NULL, M=0, q=NULL, s=NULL)) == fp8.OK  # M == 0: no-op
+    assert f(*args(M=-1)) == fp8.ERR_INVALID_ARG
+    assert f(*args(dt=7)) == fp8.ERR_INVALID_ARG
+    assert f(*args(layout=5)) == fp8.ERR_INVALID_ARG
+    assert f(*args(K=200, ld=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(M=100, layout=fp8.B_BLOCK_128x128)) == fp8.ERR_UNSUPPORTED  # weight layout: M % 128
+    assert f(*args(ld=128)) == fp8.ERR_INVALID_ARG  # ld < K
+    assert f(*args(x=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(s=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(x=BAD)) == fp8.ERR_MISALIGNED
+    assert f(*args(s=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(ld=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
 
 
 def test_quant_weight_dual_validation(L):
