@@ -121,7 +121,8 @@ class Timer:
     def __exit__(self, *a):
         self._record()
 
-    def mean_ms(self):
+    def times_ms(self):
+        """Duration of every bracketed launch, in recording order."""
         self.torch.cuda.synchronize()
         ts = []
         for i in range(0, self.used, 2):
@@ -130,7 +131,19 @@ class Timer:
             if rc != 0:
                 raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
             ts.append(ms.value)
+        return ts
+
+    def mean_ms(self):
+        ts = self.times_ms()
         return sum(ts) / len(ts) if ts else float("nan")
+
+    def percentiles_ms(self):
+        """p10, median and p90 of the bracketed launches (nearest rank)."""
+        ts = sorted(self.times_ms())
+        if not ts:
+            return None
+        pick = lambda q: ts[min(len(ts) - 1, int(q * len(ts)))]
+        return {"p10": pick(0.10), "p50": pick(0.50), "p90": pick(0.90)}
 
 
 def _cpu_threads():
@@ -222,7 +235,8 @@ def bench_dense(args, torch, fp8, workloads):
             "fp8_quant_weight_128x128": {"ms": w_ms, "GB/s": w_bytes / (w_ms * 1e-3) / 1e9,
                                          "frac_hbm": w_bytes / (w_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
             "fp8_block_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
-                               "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS},
+                               "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
+                               "ms_percentiles": t_gemm.percentiles_ms()},
         },
         "roofline": {
             "bound": "mfma",
@@ -294,7 +308,8 @@ def bench_pow2(args, torch, fp8, workloads):
         "kernels": {
             "fp8_quant_act_1x128_pow2": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
             "fp8_quant_weight_128x128_pow2": _hbm_line("w", t_w.mean_ms() / args.steps, w_bytes, {}),
-            "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
+            "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
+                                        "ms_percentiles": t_gemm.percentiles_ms()},
         },
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_FP8_TFLOPS,
@@ -642,7 +657,7 @@ def bench_moe(args, torch, fp8, workloads):
                    "T": T, "M_total": Mt, "N": N, "K": K, "G": G},
         "kernels": {
             "fp8_quant_act_1x128 (tokens)": _hbm_line("act", tq.mean_ms() / args.steps, T * K * 3 + T * (K // 128) * 4, {}),
-            "fp8_block_grouped_gemm_gather": gemm_line(gms),
+            "fp8_block_grouped_gemm_gather": dict(gemm_line(gms), ms_percentiles=tg.percentiles_ms()),
             "fp8_block_grouped_gemm (pre-permuted rows)": gemm_line(pms),
         },
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
@@ -694,7 +709,8 @@ def bench_wgrad(args, torch, fp8, workloads):
         "kernels": {
             "fp8_quant_act_1x128 (transposed, x2)": _hbm_line("q", tq.mean_ms(), qbytes, {}),
             "fp8_block_gemm (row scales, exact)": {"ms": gms, "TFLOP/s": flop / (gms * 1e-3) / 1e12,
-                                                   "frac_fp16_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS},
+                                                   "frac_fp16_peak": flop / (gms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+                                                   "ms_percentiles": tg.percentiles_ms()},
             "fp8_block_gemm (row scales, fp8 accum)": {"ms": fms, "TFLOP/s": flop / (fms * 1e-3) / 1e12,
                                                        "frac_fp8_peak": flop / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS},
         },
