@@ -33,6 +33,18 @@ def test_activation_layout():
     _check(workloads.tiny()["x"], "act", "tiny fp32 (1% x50)")
 
 
+def test_padded_row_pitch():
+    # x is the first 512 columns of a [256, 640] tensor: row pitch 640 elements
+    wide = workloads.dense(M=256, N=128, K=640)["x"]
+    x = wide.cuda()[:, :512]
+    say(f"per-tensor padded pitch {tuple(x.shape)} ld {x.stride(0)}")
+    q, s = fp8.fp8_quant_per_tensor(x)
+    torch.cuda.synchronize()
+    q_ref, s_ref = ablation.quant_per_tensor(f32(wide[:, :512].contiguous()))
+    assert_codes_equal(q, q_ref, "padded pitch")
+    assert np.all(s.cpu().numpy().view(np.uint32) == np.float32(s_ref).view(np.uint32))
+
+
 def test_weight_layout():
     _check(workloads.dense(M=1, N=384, K=1024)["w"], "weight", "weight bf16")
     _check(workloads.tiny()["w"], "weight", "tiny weight fp32")
