@@ -661,6 +661,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   int st = 0;  // stage holding block kb
   v4f P[2][SM];
   v4f sbr[2];  // row mode: row scales of the sub-tiles whose partials are pending
+  // Grouped tiles: the last sub-tile's partials are formed right after the
+  // barrier; promoting them at once would wait on those MFMAs (s_nop hazards).
+  // Their promotion is deferred to the first sub-tile step of the next block,
+  // with the block's factors kept in f_prev (P[(SN-1)&1] and sbr[(SN-1)&1] are
+  // not rewritten before then: step 0 writes the other buffer).  1.8% faster on
+  // the MoE shape; 1% slower on the dense 256 x 256 tile, which keeps the
+  // immediate promotion.
+  constexpr bool DEFER = GROUPED && !SCALED && BALIGN;
+  static_assert(!DEFER || SN % 2 == 0, "the deferred partials use the buffer step 0 does not write");
+  float f_prev[SM];
   for (int kb = 0; kb < KB; ++kb) {
     // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
     // Near the end the free stage is refilled with block KB-1, which is not read
@@ -710,7 +720,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
         if constexpr (EXACT) wn_frag = widen(fn);
 #pragma unroll
         for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
-        if (i > 0) promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
+        if (i > 0)
+          promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
+        else if (DEFER && kb > 0)
+          promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
       }
       if constexpr (FD2) {
         fn = fn1;
@@ -762,7 +775,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
     }
     promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
-    promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
+    if constexpr (DEFER) {
+#pragma unroll
+      for (int j = 0; j < SM; ++j) f_prev[j] = f_old[j];
+    } else {
+      promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
+    }
+  }
+  if constexpr (DEFER) {
+    if (KB > 0) promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
   }
   }  // live wavefront
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
