@@ -17,7 +17,8 @@
 //    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
 //  * One 128-wide K block per LDS stage; the loads of block kb+STAGES-1 are in
 //    flight while block kb is multiplied.  They are issued over the first six
-//    of the eight sub-tile steps (first two of four for 128 x 256), one or two
+//    of the eight sub-tile steps (128 x 256 tiles: the first three of four when
+//    grouped, else the first two), one or two
 //    DMAs per step between MFMAs: early enough to land before the end of the
 //    iteration, spread out because each DMA costs the issuing wavefront and the
 //    LDS both per instruction and per byte.
