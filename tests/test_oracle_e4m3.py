@@ -115,3 +115,51 @@ def test_encode_never_nan_code():
     x = _probe_points() * np.float32(3.0)
     c = e4m3.encode(x)
     assert not np.any((c & 0x7F) == 0x7F)
+
+
+def test_encode_exhaustive_against_torch_thresholds():
+    """Every non-negative fp32 up to 464 (and its negation), through torch's codec.
+
+    torch's codes over all 1.14e9 bit patterns in [0, 464] form a staircase with
+    unit steps; the oracle's encoder is monotone by construction (a search over
+    increasing midpoints), so it equals torch on the whole range exactly when it
+    switches codes at the same 126 fp32 values.  Beyond 464 torch gives NaN and
+    the oracle saturates (checked in test_spec_values)."""
+    top = int(np.float32(464.0).view(np.uint32))
+    chunk = 1 << 27
+    first = {}  # code -> first bit pattern carrying it
+    prev_code = None
+    for lo in range(0, top + 1, chunk):
+        hi = min(lo + chunk, top + 1)
+        bits = torch.arange(lo, hi, dtype=torch.int32)
+        for sign in (0, 1):
+            x = bits.view(torch.float32)
+            if sign:
+                x = -x
+            c = x.to(torch.float8_e4m3fn).view(torch.uint8)
+            if sign:
+                assert bool(torch.all((c & 0x80) == 0x80)), "negative inputs keep the sign bit"
+                c = c & 0x7F
+                assert bool(torch.all(c == pos)), "torch's codec is sign-symmetric"
+                continue
+            pos = c
+            step = c[1:].to(torch.int16) - c[:-1].to(torch.int16)
+            assert int(step.min()) >= 0 and int(step.max()) <= 1, "unit staircase"
+            if prev_code is not None:
+                assert 0 <= int(c[0]) - prev_code <= 1
+                if int(c[0]) != prev_code:
+                    first[int(c[0])] = lo
+            else:
+                assert int(c[0]) == 0
+            for k in torch.nonzero(step).flatten().tolist():
+                first[int(c[k + 1])] = lo + k + 1
+            prev_code = int(c[-1])
+    assert sorted(first) == list(range(1, 0x7F)), "every code 1 .. 0x7E is reached"
+    thr = np.array([first[c] for c in range(1, 0x7F)], dtype=np.uint32)
+    below = (thr - 1).view(np.float32)
+    at = thr.view(np.float32)
+    codes = np.arange(1, 0x7F, dtype=np.uint8)
+    assert np.array_equal(e4m3.encode(at), codes)
+    assert np.array_equal(e4m3.encode(below), codes - 1)
+    assert np.array_equal(e4m3.encode(-at), codes | 0x80)
+    assert np.array_equal(e4m3.encode(-below), (codes - 1) | 0x80)
