@@ -175,6 +175,38 @@ def test_weight_dual_small():
     _weight_dual(torch.from_numpy(_special_tiles()[:8].reshape(8, 1024).repeat(16, axis=0)[:128]), "special")
 
 
+def test_cast_exhaustive_through_the_act_quantiser():
+    """Every fp32 in [0, 448] and its negation through the 1x128 kernel's cast.
+
+    Each tile holds +-448 followed by 127 probe values, so amax = 448, s = 1 and
+    1/s = 1: the kernel casts the probe values unscaled.  The expected codes come
+    from torch's CPU float8_e4m3fn codec, which the oracle pins (tests/
+    test_oracle_e4m3.py) show equal to the oracle's encoder on this whole range."""
+    top = int(np.float32(448.0).view(np.uint32))
+    per = 127
+    tiles_per_call = 1 << 20
+    total = top + 1
+    for sign in (1.0, -1.0):
+        say(f"cast sweep, sign {sign:+.0f}: {total} values in tiles of 448 + 127 probes")
+        for lo in range(0, total, tiles_per_call * per):
+            n = min(tiles_per_call * per, total - lo)
+            T = (n + per - 1) // per
+            bits = torch.clamp(torch.arange(lo, lo + T * per, dtype=torch.int32), max=top)
+            vals = bits.view(torch.float32) * sign
+            x = torch.empty((T, 128), dtype=torch.float32)
+            x[:, 0] = 448.0 * sign
+            x[:, 1:] = vals.view(T, per)
+            q, s = fp8.fp8_quant_act_1x128(x.cuda())
+            got = q[:, 1:].reshape(-1).cpu()
+            torch.cuda.synchronize()
+            assert bool(torch.all(s == 1.0)), "scale of an amax-448 tile"
+            assert bool(torch.all(q[:, 0] == (0x7E if sign > 0 else 0xFE)))
+            want = vals.to(torch.float8_e4m3fn).view(torch.uint8)
+            if not torch.equal(got, want):
+                bad = torch.nonzero(got != want).flatten()[:5].tolist()
+                raise AssertionError([(float(vals[i]), hex(int(got[i])), hex(int(want[i]))) for i in bad])
+
+
 def test_validation_errors_reported():
     x = torch.zeros((4, 100), device="cuda")
     with pytest.raises(fp8.Fp8fgError) as e:
