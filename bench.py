@@ -387,23 +387,27 @@ def bench_fused(args, torch, fp8, workloads):
     }
 
 
-def cpu_baseline_dense(d):
-    """The oracle on the dense step itself (all 4096 rows of X, all of W): a few
-    seconds to tens of seconds of host time, depending on the host's cores."""
+def cpu_baseline_dense(d, min_seconds=10.0, max_steps=10):
+    """The oracle on the dense step itself (all 4096 rows of X, all of W),
+    repeated until at least `min_seconds` of host time (at most `max_steps`
+    steps): a few seconds per step, depending on the host's cores."""
     from oracle import gemm, quant
 
     rows = d["x"].shape[0]
     x = d["x"][:rows].float().numpy()
     w = d["w"].float().numpy()
-    t0 = time.perf_counter()
-    ra, rsa = quant.quant_1x128(x)
-    rb, rsb = quant.quant_128x128(w)
-    gemm.block_gemm(ra, rsa, rb, rsb)
-    dt = time.perf_counter() - t0
-    flop = 2.0 * rows * w.shape[0] * w.shape[1]
+    steps, dt = 0, 0.0
+    while steps < max_steps and (steps == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        ra, rsa = quant.quant_1x128(x)
+        rb, rsb = quant.quant_128x128(w)
+        gemm.block_gemm(ra, rsa, rb, rsb)
+        dt += time.perf_counter() - t0
+        steps += 1
+    flop = 2.0 * rows * w.shape[0] * w.shape[1] * steps
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"one dense step, X [{rows},7168] and W [7168,7168]: numpy 1x128 + 128x128 "
-                      f"quantisation (one thread) and fp64 GEMM (BLAS threads); {dt:.1f} s"}
+            "sample": f"{steps} dense step(s), X [{rows},7168] and W [7168,7168]: numpy 1x128 + 128x128 "
+                      f"quantisation (one thread) and fp64 GEMM (BLAS threads); {dt:.1f} s in all"}
 
 
 # ------------------------------------------------------------------ other rows
