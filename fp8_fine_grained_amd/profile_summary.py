@@ -221,6 +221,13 @@ def mfma(csv_path, substr, last_n, kernel_src, out_md, command):
                 lines.append(f"| {k} / SQ_WAVE_CYCLES | {avg[k] / wc:.3f} |")
         lines.append(f"| resident wavefronts per SIMD = 4 x SQ_WAVE_CYCLES / (active cycles x {SIMDS}) | "
                      f"{4 * wc / (active * SIMDS):.2f} |")
+    if avg.get("SQ_INSTS_MFMA"):
+        if "SQ_INSTS_VALU" in avg:
+            lines.append(f"| VALU instructions per MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA | "
+                         f"{avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f} |")
+    if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+        lines.append(f"| VALU co-execution = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES | "
+                     f"{avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.3f} |")
     if flops8:
         lines.append(f"| FP8 matrix-core work = MOPS_F8 x 512 | {flops8 / 1e9:.1f} GFLOP, {flops8 / t_s / 1e12:.0f} TFLOP/s |")
     if flops16:
