@@ -14,7 +14,7 @@ cannot serve the quantisers' reads from one step to the next.
 Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused``) measure the remaining rows of
 the path and print their own JSON line; the default run prints exactly one line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2|fused]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor]
                     [--no-cpu-baseline]
 """
 
@@ -406,7 +406,7 @@ def cpu_baseline_dense(d, min_seconds=10.0, max_steps=10):
         steps += 1
     flop = 2.0 * rows * w.shape[0] * w.shape[1] * steps
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"{steps} dense step(s), X [{rows},7168] and W [7168,7168]: numpy 1x128 + 128x128 "
+            "sample": f"{steps} dense step(s), X [{rows},{x.shape[1]}] and W [{w.shape[0]},{w.shape[1]}]: numpy 1x128 + 128x128 "
                       f"quantisation (one thread) and fp64 GEMM (BLAS threads); {dt:.1f} s in all"}
 
 
