@@ -90,7 +90,9 @@ def stats(csv_path, out_md, command, bench_log=None):
         lines += ["", "bench.py's own HIP-event averages over the same timed steps (the first table also",
                   "counts the warm-up launches):", "", "| launch | ms |", "|---|---|"]
         for name, k in bench.get("kernels", {}).items():
-            lines.append(f"| {name} | {k['ms']:.4f} |")
+            ms = k["ms"] if "ms" in k else (k["us"] / 1e3 if "us" in k else None)
+            if ms is not None:
+                lines.append(f"| {name} | {ms:.4f} |")
         lines.append(f"| whole step | {bench['ms_per_step']:.4f} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
