@@ -149,10 +149,16 @@ __device__ __forceinline__ WideFrag widen(const v8i& f) {
 // at the wave-uniform byte address `lds`.  The tile form takes a wave-uniform
 // base (SGPR pair) plus a fixed 32-bit per-lane offset, so advancing to the
 // next K block is a scalar add and the instruction reads one address VGPR.
-// M0 is written here and nowhere else in the kernel (no other instruction of
-// this kernel reads M0), so it needs no saving.
+// The LDS address is taken from M0, which the DMA may read only one wait state
+// after a scalar ALU write (gfx9 hazard; the compiler places the same s_nop 0
+// for its own LDS-DMA builtin, but cannot see inside this asm).  M0 is a
+// reserved register to the compiler, so it cannot be listed as clobbered; the
+// compiled kernels name M0 nowhere but in these helpers and have no other
+// instruction that reads it (both checked on the gfx950 assembly by the
+// library's static device-code test), so writing it here disturbs nothing.
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+               : "memory");
 }
 // The same with only the lanes of `mask` active.  The instruction is always
 // issued (no branch around it), so every wavefront's count of outstanding
@@ -169,6 +175,7 @@ __device__ __forceinline__ void dma16_masked(const uint8_t* base, uint32_t voff,
       "s_mov_b64 %0, exec\n\t"
       "s_mov_b64 exec, %4\n\t"
       "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b64 exec, %0"
       : "=&s"(saved)
@@ -176,7 +183,7 @@ __device__ __forceinline__ void dma16_masked(const uint8_t* base, uint32_t voff,
       : "memory");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory");
 }
 // Wait until at most N of this wavefront's loads are outstanding (those of the
 // newer blocks) and all of its LDS reads have completed, then
