@@ -824,7 +824,7 @@ def main():
         copy_calibration(args, torch)
         return
     import fp8_fine_grained_amd.binding as fp8
-    from fp8_fine_grained_amd import workloads
+    import workloads
 
     fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
           "dgrad": bench_dgrad, "pow2": bench_pow2,

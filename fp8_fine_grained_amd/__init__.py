@@ -3,8 +3,8 @@ FP8 GEMM for AMD MI355X (gfx950).
 
 The product is the C-ABI library ``libfp8fg.so`` (include/fp8fg.h) built from
 ``csrc/``; :mod:`fp8_fine_grained_amd.binding` calls it from Python with
-torch tensors as device memory.  :mod:`fp8_fine_grained_amd.workloads` draws
-the seeded synthetic inputs.
+torch tensors as device memory.  The seeded synthetic inputs come from the
+top-level ``workloads`` module, outside this package.
 """
 
 from .binding import (  # noqa: F401

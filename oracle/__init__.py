@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may use it.  It shares no code, tables or helpers with the HIP
 library under ``fp8_fine_grained_amd/csrc``; the two meet only at the seeded
-input generators (``fp8_fine_grained_amd.workloads``), which hold none of the
+input generators (the top-level ``workloads`` module, which imports nothing
+from the product package), which hold none of the
 method's arithmetic.
 
 Sources (the four web pages this work follows; each is cited by title and

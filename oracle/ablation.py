@@ -18,10 +18,18 @@ This module quantises the same inputs both ways and measures the damage.
 * :func:`gemm_error` -- relative Frobenius error of the fp64 product of the
   dequantised operands against the fp64 product of the unquantised ones.
 
-Parity: the per-tensor quantiser is pinned in tests/test_oracle_ablation.py
-(a tensor that is one 1x128 tile quantises exactly as quant_1x128; 2^j and
-sign equivariance; the amax element maps to 0x7E); the statistics are plain
-definitions evaluated in fp64.
+* :func:`subnormal_fraction` -- the fraction of nonzero inputs whose code
+  lies below E4M3's normal range (exponent field 0: zero or subnormal).
+
+Parity (tests/test_oracle_ablation.py): the per-tensor quantiser is pinned by
+a tensor that is one 1x128 tile (it quantises exactly as quant_1x128), 2^j
+and sign equivariance and the amax element mapping to 0x7E.  Every function
+here -- quant_per_tensor, dequant_per_tensor, qdq_stats, subnormal_fraction,
+gemm_error, and the dequantisers of oracle.quant they are used with -- is
+pinned by tests/golden/ablation_handworked.json: a 2x128 tensor with an
+ordinary tile and a 64x outlier tile and a two-row weight, whose codes,
+dequantised values, element-wise relative errors, statistics and GEMM errors
+were worked out by hand as exact fractions.
 """
 
 import numpy as np
@@ -52,7 +60,6 @@ def qdq_stats(x, deq):
         "rel_p99": float(np.percentile(rel, 99)),
         "rel_mean": float(np.mean(rel)),
         "flushed_to_zero": float(np.mean(deq[nz] == 0)),
-        # below E4M3's normal range: |code value| < 2^-6, i.e. |deq| < 2^-6 * scale
         "frac_nonzero": float(np.mean(nz)),
     }
 
@@ -104,7 +111,7 @@ def main():
     activations of the quantiser workload (1024 of the 16384 rows)."""
     import json
 
-    from fp8_fine_grained_amd import workloads
+    import workloads
 
     d = workloads.dense(M=512)
     res = {"dense_projection_512x7168x7168": compare(d["x"].float().numpy(), d["w"].float().numpy())}

@@ -17,7 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from fp8_fine_grained_amd import binding as fp8, workloads
+import workloads
+from fp8_fine_grained_amd import binding as fp8
 from oracle import e4m3, gemm, quant
 from tests.gpu_util import check_guard, f32, fp8_mfma_bound, guarded, say
 

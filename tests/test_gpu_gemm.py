@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from fp8_fine_grained_amd import binding as fp8, workloads
+import workloads
+from fp8_fine_grained_amd import binding as fp8
 from oracle import gemm, quant
 from tests.gpu_util import check_bf16, check_f32, check_guard, f32, fp8_mfma_bound, frob_rel, guarded, say
 

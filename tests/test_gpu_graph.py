@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from fp8_fine_grained_amd import binding as fp8, workloads
+import workloads
+from fp8_fine_grained_amd import binding as fp8
 from oracle import gemm, quant
 from tests.gpu_util import check_f32, f32, say
 

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 import torch
 
-from fp8_fine_grained_amd import binding as fp8, workloads
+import workloads
+from fp8_fine_grained_amd import binding as fp8
 from oracle import ablation, gemm
 from tests.gpu_util import assert_codes_equal, check_bf16, f32, say
 

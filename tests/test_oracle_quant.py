@@ -8,7 +8,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from fp8_fine_grained_amd import workloads
+import workloads
 from oracle import e4m3, quant
 from tests.exact import e4m3_values_torch, round_f32
 
