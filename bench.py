@@ -7,9 +7,14 @@ W bf16 [7168,7168] (N(0,0.02)):
     fp8_quant_act_1x128(X) -> fp8_quant_weight_128x128(W) -> fp8_block_gemm -> Y bf16
 The metric is GEMM TFLOP/s of the whole step (2*M*N*K / step time, host clock
 over the timed steps); within those steps each GEMM launch sits between two HIP
-events on its stream, and the quantisers are timed afterwards as batches.  The three
-inputs are rotated over three HBM copies so that the 256 MB last-level cache
-cannot serve the quantisers' reads from one step to the next.
+events on its stream, and the quantisers are timed afterwards as batches.  X and
+W are rotated over enough HBM copies (6 of X, 3 of W) that a pass over them
+exceeds the 256 MB last-level cache, which so never serves a quantiser's reads.
+The line also times, outside the step, the quantisers at the shapes their HBM
+target is quoted on (activation [16384,7168], weight [7168,18432]) and the
+dual weight quantiser, each rotated the same way.  Before the W warm-up steps
+the step runs back to back for --settle seconds (default 1): a cold GPU's
+clocks take ~100 GEMMs to come up, which a long training run never sees.
 
 Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused``) measure the remaining rows of
 the path and print their own JSON line; the default run prints exactly one line.
@@ -146,14 +151,51 @@ class Timer:
         return {"p10": pick(0.10), "p50": pick(0.50), "p90": pick(0.90)}
 
 
-def _cpu_threads():
+LLC_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+
+
+def _copies(nbytes, least=3):
+    """Input copies to rotate over so that one pass over them exceeds the
+    last-level cache by a margin: a launch never finds its input there."""
+    return max(least, -(-int(1.25 * LLC_BYTES) // int(nbytes)))
+
+
+def _cpu_info():
+    """Host CPU model and the threads the oracle runs on: its quantisers use
+    one thread per core this process may run on (sched_getaffinity), its GEMM
+    the BLAS library's thread pool."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
 
-        n = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
     except Exception:
-        n = 1
-    return int(n)
+        blas = None
+    return model, len(os.sched_getaffinity(0)), blas
+
+
+def settle_clocks(torch, step, seconds):
+    """Run `step` back to back for `seconds` of wall time before the warm-up
+    steps.  From a cold start the GPU's clocks take ~100 dense GEMMs (about a
+    fifth of a second) to come up; what the timed steps measure is the steady
+    rate of a long training run, which never sees that ramp."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        step(n, False)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return n
 
 
 # ------------------------------------------------------------------ dense
@@ -161,8 +203,9 @@ def _cpu_threads():
 def bench_dense(args, torch, fp8, workloads):
     M, N, K = 4096, 7168, 7168
     d = workloads.dense()
-    xs = [d["x"].cuda() for _ in range(3)]
-    ws = [d["w"].cuda() for _ in range(3)]
+    nx, nw = _copies(M * K * 2), _copies(N * K * 2)
+    xs = [d["x"].cuda() for _ in range(nx)]
+    ws = [d["w"].cuda() for _ in range(nw)]
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
@@ -172,7 +215,7 @@ def bench_dense(args, torch, fp8, workloads):
     t_act, t_w = Timer(torch, 1), Timer(torch, 1)
 
     def step(i, timed):
-        x, w = xs[i % 3], ws[i % 3]
+        x, w = xs[i % nx], ws[i % nw]
         fp8.fp8_quant_act_1x128(x, qa, sa)
         fp8.fp8_quant_weight_128x128(w, qb, sb)
         if timed:
@@ -181,6 +224,7 @@ def bench_dense(args, torch, fp8, workloads):
         else:
             fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
 
+    settled = settle_clocks(torch, step, args.settle)
     for i in range(args.warmup):
         step(i, False)
     # The timed steps: the GEMM launch of each step sits between two events (the
@@ -197,11 +241,12 @@ def bench_dense(args, torch, fp8, workloads):
     # few microseconds to these short kernels).
     with t_act:
         for i in range(args.steps):
-            fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
+            fp8.fp8_quant_act_1x128(xs[i % nx], qa, sa)
     with t_w:
         for i in range(args.steps):
-            fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+            fp8.fp8_quant_weight_128x128(ws[i % nw], qb, sb)
     torch.cuda.synchronize()
+    extra = quantiser_lines(args, torch, fp8, workloads, d)
     flop = 2.0 * M * N * K
     gemm_ms = t_gemm.mean_ms()
     act_ms, w_ms = t_act.mean_ms() / args.steps, t_w.mean_ms() / args.steps
@@ -227,7 +272,8 @@ def bench_dense(args, torch, fp8, workloads):
             "workload": "dense projection: quantise X bf16 [4096,7168] per 1x128 and W bf16 [7168,7168] "
                         "per 128x128 to E4M3, then block-scaled FP8 GEMM Y = X W^T, bf16 out, "
                         "FP8 matrix-core accumulation promoted to fp32 every 128 K",
-            "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": 3,
+            "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": {"X": nx, "W": nw},
+            "clock_settle_s": args.settle, "clock_settle_steps": settled,
         },
         "kernels": {
             "fp8_quant_act_1x128": {"ms": act_ms, "GB/s": act_bytes / (act_ms * 1e-3) / 1e9,
@@ -237,6 +283,7 @@ def bench_dense(args, torch, fp8, workloads):
             "fp8_block_gemm": {"ms": gemm_ms, "TFLOP/s": gemm_tflops,
                                "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS,
                                "ms_percentiles": t_gemm.percentiles_ms()},
+            **extra,
         },
         "roofline": {
             "bound": "mfma",
@@ -278,6 +325,7 @@ def bench_pow2(args, torch, fp8, workloads):
         else:
             fp8.fp8_block_gemm(qa, sa, qb, sb, accum="scaled", y=y)
 
+    settle_clocks(torch, step, args.settle)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -346,6 +394,7 @@ def bench_fused(args, torch, fp8, workloads):
         else:
             fp8.fp8_block_gemm_quant(qa, sa, qb, sb, q=qy, scales=sy)
 
+    settle_clocks(torch, step, args.settle)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -387,6 +436,57 @@ def bench_fused(args, torch, fp8, workloads):
     }
 
 
+def quantiser_lines(args, torch, fp8, workloads, d):
+    """The quantisers at the shapes their HBM target is quoted on (activation
+    bf16 [16384,7168] Student-t, weight bf16 [7168,18432] N(0,0.02)), and the
+    dual weight quantiser of the data gradient on W [7168,7168]; each timed as
+    one back-to-back batch over enough rotated input copies that a pass over
+    them exceeds the last-level cache.  Not part of the step or its value."""
+    act = workloads.quant_act()
+    w = workloads.quant_weight()
+    M, K = act.shape
+    N, KW = w.shape
+    na, nw = _copies(act.numel() * 2, 2), _copies(w.numel() * 2, 2)
+    acts = [act.cuda() for _ in range(na)]
+    ws = [w.cuda() for _ in range(nw)]
+    del act, w
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qw = torch.empty((N, KW), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((N // 128, KW // 128), dtype=torch.float32, device="cuda")
+    D = d["w"].shape[0]
+    nd = _copies(D * D * 2)
+    wd = [d["w"].cuda() for _ in range(nd)]
+    q1 = torch.empty((D, D), dtype=torch.uint8, device="cuda")
+    q2 = torch.empty((D, D), dtype=torch.uint8, device="cuda")
+    s1 = torch.empty((D // 128, D // 128), dtype=torch.float32, device="cuda")
+    s2 = torch.empty((D // 128, D // 128), dtype=torch.float32, device="cuda")
+    n = max(args.steps, 20)
+    for i in range(max(args.warmup, 4)):
+        fp8.fp8_quant_act_1x128(acts[i % na], qa, sa)
+        fp8.fp8_quant_weight_128x128(ws[i % nw], qw, sw)
+        fp8.fp8_quant_weight_128x128_dual(wd[i % nd], q1, s1, q2, s2)
+    ta, tw, tdl = Timer(torch, 1), Timer(torch, 1), Timer(torch, 1)
+    with ta:
+        for i in range(n):
+            fp8.fp8_quant_act_1x128(acts[i % na], qa, sa)
+    with tw:
+        for i in range(n):
+            fp8.fp8_quant_weight_128x128(ws[i % nw], qw, sw)
+    with tdl:
+        for i in range(n):
+            fp8.fp8_quant_weight_128x128_dual(wd[i % nd], q1, s1, q2, s2)
+    torch.cuda.synchronize()
+    ab = M * K * 3 + M * (K // 128) * 4
+    wb = N * KW * 3 + (N // 128) * (KW // 128) * 4
+    db = D * D * 4 + 2 * (D // 128) ** 2 * 4
+    return {
+        "fp8_quant_act_1x128 [16384,7168] Student-t": _hbm_line("act", ta.mean_ms() / n, ab, {"copies": na}),
+        "fp8_quant_weight_128x128 [7168,18432]": _hbm_line("w", tw.mean_ms() / n, wb, {"copies": nw}),
+        "fp8_quant_weight_128x128_dual [7168,7168]": _hbm_line("dual", tdl.mean_ms() / n, db, {"copies": nd}),
+    }
+
+
 def cpu_baseline_dense(d, min_seconds=10.0, max_steps=10):
     """The oracle on the dense step itself (all 4096 rows of X, all of W),
     repeated until at least `min_seconds` of host time (at most `max_steps`
@@ -405,9 +505,12 @@ def cpu_baseline_dense(d, min_seconds=10.0, max_steps=10):
         dt += time.perf_counter() - t0
         steps += 1
     flop = 2.0 * rows * w.shape[0] * w.shape[1] * steps
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": _cpu_threads(), "kind": "oracle",
-            "sample": f"{steps} dense step(s), X [{rows},{x.shape[1]}] and W [{w.shape[0]},{w.shape[1]}]: numpy 1x128 + 128x128 "
-                      f"quantisation (one thread) and fp64 GEMM (BLAS threads); {dt:.1f} s in all"}
+    model, cores, blas = _cpu_info()
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": model, "blas_threads": blas,
+            "sample": f"{steps} dense step(s), X [{rows},{x.shape[1]}] and W [{w.shape[0]},{w.shape[1]}]: numpy 1x128 + "
+                      f"128x128 quantisation ({quant.threads()} threads over row chunks) and fp64 GEMM (BLAS, "
+                      f"{blas} threads); {dt:.1f} s in all"}
 
 
 # ------------------------------------------------------------------ other rows
@@ -750,6 +853,7 @@ def bench_dgrad(args, torch, fp8, workloads):
         else:
             fp8.fp8_block_gemm(qa, sa, qt, st, accum="fp8", y=y)
 
+    settle_clocks(torch, step, args.settle)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -806,6 +910,9 @@ def main():
     # The first ~100 dense GEMMs of a process run up to 25% slower while the
     # clocks ramp up; the default warm-up covers that ramp.
     ap.add_argument("--warmup", type=int, default=100)
+    # Back-to-back steps before the warm-up, by wall time: the clock ramp of a
+    # cold GPU is not part of a training step's steady rate.
+    ap.add_argument("--settle", type=float, default=1.0, help="seconds of untimed steps before the warm-up")
     ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused", "tiny", "pertensor"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")

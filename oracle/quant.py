@@ -57,11 +57,43 @@ identity on E4M3-exact tiles, group locality, and the fp32 rounding of each
 step against exact rational arithmetic.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from .e4m3 import E4M3_MAX, encode
 
 GROUP = 128
+#: Rows per work item when a quantiser splits its input over threads (a
+#: multiple of 128, so a chunk holds whole 128x128 weight blocks).
+CHUNK_ROWS = 512
+
+
+def threads():
+    """Host threads the oracle uses: the cores this process may run on."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _by_row_chunks(one, x, scale, group_rows):
+    """Run the quantiser ``one`` on consecutive row chunks of ``x`` in threads.
+
+    Groups never straddle a chunk (chunks are whole multiples of the group
+    height), so the result is the same as one call over all rows: the chunks
+    only divide the work.  numpy releases the interpreter lock inside its
+    array operations, so the threads run in parallel."""
+    assert CHUNK_ROWS % group_rows == 0
+    n = x.shape[0]
+    nt = threads()
+    if nt == 1 or n <= CHUNK_ROWS:
+        return one(x, scale)
+    starts = list(range(0, n, CHUNK_ROWS))
+    with ThreadPoolExecutor(min(nt, len(starts))) as ex:
+        parts = list(ex.map(lambda r0: one(x[r0:r0 + CHUNK_ROWS], scale), starts))
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
 def _scale_and_inverse(amax):
@@ -112,9 +144,13 @@ def quant_1x128(x, scale="amax"):
     [M, ceil(K/128)], where ``s[m, g]`` belongs to columns
     ``128*g .. 128*g+127`` of row ``m`` (a ragged last group covers the
     columns present).  ``scale="pow2"`` takes power-of-two scales.
+    Large inputs are split into row chunks quantised in parallel threads.
     """
+    return _by_row_chunks(_quant_1x128, _check_input(x), scale, 1)
+
+
+def _quant_1x128(x, scale):
     scale_and_inverse = _SCALES[scale]
-    x = _check_input(x)
     M, K = x.shape
     G = -(-K // GROUP)
     q = np.empty((M, K), dtype=np.uint8)
@@ -135,10 +171,14 @@ def quant_128x128(w, scale="amax"):
     Returns ``(q, s)``: uint8 codes [N, K] and fp32 scales
     [ceil(N/128), ceil(K/128)], where ``s[i, j]`` belongs to rows
     ``128*i ..`` and columns ``128*j ..`` of ``w``.  ``scale="pow2"`` takes
-    power-of-two scales.
+    power-of-two scales.  Large inputs are split into chunks of whole block
+    rows quantised in parallel threads.
     """
+    return _by_row_chunks(_quant_128x128, _check_input(w), scale, GROUP)
+
+
+def _quant_128x128(w, scale):
     scale_and_inverse = _SCALES[scale]
-    w = _check_input(w)
     N, K = w.shape
     GN, GK = -(-N // GROUP), -(-K // GROUP)
     q = np.empty((N, K), dtype=np.uint8)

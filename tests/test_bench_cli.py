@@ -41,5 +41,15 @@ def test_cpu_baseline_fields():
          "w": (torch.randn(256, 256, generator=g) * 0.02).to(torch.bfloat16)}
     out = bench.cpu_baseline_dense(d, min_seconds=0.0, max_steps=2)
     assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
-    assert out["value"] > 0 and out["cores"] >= 1
+    assert out["value"] > 0 and out["cores"] == len(os.sched_getaffinity(0))
+    assert out["cpu_model"] and out["cpu_model"] != "unknown"
     assert out["sample"].startswith("1 dense step(s)")
+
+
+def test_rotated_copies_exceed_the_last_level_cache():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    for nbytes in (4096 * 7168 * 2, 7168 * 7168 * 2, 16384 * 7168 * 2, 7168 * 18432 * 2):
+        n = bench._copies(nbytes, 2)
+        assert n >= 2 and n * nbytes > bench.LLC_BYTES

@@ -138,9 +138,11 @@ def test_dgrad_small(M, N, K):
     check_f32(_run(g, M, K, torch.float32, "exact"), ref, "exact accum fp32")
 
 
-def _sample_rows(M, n, seed):
+def _sample_rows(M, n, seed, tile=256):
+    """The first and the last row of every `tile`-row m-tile, plus n random rows."""
     rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], rng.choice(M, size=n, replace=False)]))
+    edges = [r for t0 in range(0, M, tile) for r in (t0, min(M, t0 + tile) - 1)]
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 1], edges, rng.choice(M, size=n, replace=False)]))
     return rows
 
 
@@ -161,20 +163,55 @@ def test_full_dense_projection():
     assert torch.isfinite(y.float()).all()
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(600)
 def test_full_wgrad():
+    """7168 x 7168 x 16384 with fp32 output in both accumulation modes.  The
+    sampled rows are the first and last of every 256-row m-tile plus random
+    ones; over all 7168 columns they meet every tile, the K-split tiles of the
+    partial last round included (with FP8 accumulation, 784 tiles of 256 x
+    256: tiles 768-783, m-tiles 24-27 x n-tiles 24-27, each in 16 K parts
+    that add into the zeroed output)."""
     d = workloads.wgrad()
     say("wgrad 7168x7168x16384: transposed quantisation + row-scaled GEMM on GPU")
     qa, sa = fp8.fp8_quant_act_1x128(d["dy"].cuda().t())
     qb, sb = fp8.fp8_quant_act_1x128(d["x"].cuda().t())
-    y = fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", out_dtype=torch.float32)
+    y = fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", accum="exact", out_dtype=torch.float32)
+    y8 = fp8.fp8_block_gemm(qa, sa, qb, sb, b_scale_mode="row", accum="fp8", out_dtype=torch.float32)
     torch.cuda.synchronize()
     rows = _sample_rows(7168, 12, 2)
     rb, rsb = quant.quant_1x128_along_rows(f32(d["x"]))
     assert np.array_equal(qb.cpu().numpy(), rb)
     ra, rsa = quant.quant_1x128_along_rows(f32(d["dy"][:, rows]))
-    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    trows = torch.from_numpy(rows).cuda()
+    assert np.array_equal(qa[trows].cpu().numpy(), ra)
     ref = gemm.block_gemm(ra, rsa, rb, rsb, mode="row")
-    check_f32(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows, exact accumulation")
+    check_f32(y[trows], ref, f"{rows.size} sampled rows, exact accumulation")
+    say("  FP8 matrix-core accumulation: per-element bound")
+    g8 = f32(y8[trows]).astype(np.float64)
+    bound = fp8_mfma_bound(ra, rsa, rb, rsb, "row")
+    say(f"  fp8 accumulation, {rows.size} sampled rows: Frobenius {frob_rel(g8, ref):.3e} (the stated fp32 "
+        f"target is 1e-5; only exact accumulation is held to it), max err/bound {np.max(np.abs(g8 - ref) / bound):.3f}")
+    assert np.all(np.isfinite(g8)) and np.all(np.abs(g8 - ref) <= bound)
+
+
+def test_wgrad_row_fp8_k_split_tail():
+    """Row-scaled B, FP8 accumulation, fp32 output, on a shape whose tiles fill
+    the 256 CUs once and leave a partial round: 4352 x 4096 is 272 tiles of
+    256 x 256, so the last 16 (m-tile 16, every n-tile: the last 256 rows)
+    run as min(256/16, 1024/128) = 8 K parts adding into the zeroed output."""
+    M, N, T = 4352, 4096, 1024
+    g, r = _wgrad_ops(T, M, N)
+    ref = gemm.block_gemm(*r, mode="row")
+    say(f"wgrad-shaped {M}x{N}x{T}, row-scaled B, fp32 out")
+    check_f32(_run(g, M, N, torch.float32, "exact", "row"), ref, "exact accumulation")
+    y8 = f32(_run(g, M, N, torch.float32, "fp8", "row")).astype(np.float64)
+    rows = slice(M - 256, M)
+    bound = fp8_mfma_bound(r[0][rows], r[1][rows], r[2], r[3], "row")
+    say(f"  fp8 accumulation: Frobenius {frob_rel(y8, ref):.3e} (fp32 target 1e-5 is for exact accumulation); "
+        f"last 256 rows max err/bound {np.max(np.abs(y8[rows] - ref[rows]) / bound):.3f}")
+    assert np.all(np.abs(y8[rows] - ref[rows]) <= bound)
+    check_bf16(y8, ref, "fp8 accumulation, all rows (bf16 tolerance)")
 
 
 def test_full_dgrad():

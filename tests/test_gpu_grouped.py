@@ -138,7 +138,18 @@ def test_empty_inputs_are_noops():
     assert y.shape == (0, N)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
 def test_full_moe_up_projection():
+    """Full MoE size; the first and the last row of every expert's segment (and
+    one row inside it) against the oracle, which quantises all 256 expert
+    weights itself (in spawned worker processes, one expert each)."""
+    import hashlib
+    import multiprocessing
+    import os
+
+    from tests.moe_reference import expert_reference
+
     say("MoE up-projection: 8192 tokens, 256 experts top-8, W [2048,7168] per expert")
     route = workloads.moe_routing()
     tokens = workloads.moe_tokens()
@@ -150,30 +161,37 @@ def test_full_moe_up_projection():
     xa = tokens.cuda()[perm.cuda()]
     qa, sa = fp8.fp8_quant_act_1x128(xa)
     wd = w.cuda()
+    del w
     qb, sb = fp8.fp8_quant_weight_128x128(wd.view(256 * 2048, 7168))
     del wd
     qb, sb = qb.view(256, 2048, 7168), sb.view(256, 16, 56)
     y = fp8.fp8_block_grouped_gemm(qa, sa, torch.from_numpy(offsets).cuda(), qb, sb)
     torch.cuda.synchronize()
-    sizes = np.diff(offsets)
     rng = np.random.default_rng(3)
-    experts = sorted({0, 255, int(np.argmax(sizes)), int(np.argmin(sizes)), *rng.choice(256, 6, replace=False).tolist()})
-    rows = []
-    for e in experts:
+    seg_rows = {}
+    for e in range(256):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        rows += [lo, hi - 1, int(rng.integers(lo, hi))]
-    rows = np.array(sorted(set(rows)))
-    say(f"  oracle on experts {experts}, {rows.size} rows")
+        if hi > lo:
+            seg_rows[e] = sorted({lo, hi - 1, int(rng.integers(lo, hi))})
+    rows = np.array(sorted(r for rs in seg_rows.values() for r in rs))
     ra, rsa = quant.quant_1x128(f32(tokens[perm[rows]]))
     assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
+    pos = {int(r): i for i, r in enumerate(rows)}
+    jobs = [(e, ra[[pos[r] for r in rs]], rsa[[pos[r] for r in rs]]) for e, rs in seg_rows.items()]
+    nproc = max(1, min(16, len(os.sched_getaffinity(0))))
+    say(f"  oracle: {len(jobs)} experts in {nproc} worker processes, {rows.size} rows")
+    results = []
+    with multiprocessing.get_context("spawn").Pool(nproc) as pool:
+        for r in pool.imap_unordered(expert_reference, jobs):
+            results.append(r)
+            if len(results) % 32 == 0:
+                say(f"  oracle: {len(results)} of {len(jobs)} experts done")
     ref = np.zeros((rows.size, 2048))
-    expert_of = np.searchsorted(offsets, rows, side="right") - 1
-    for e in experts:
-        qe, se = quant.quant_128x128(f32(w[e]))
-        assert np.array_equal(qb[e].cpu().numpy(), qe)
-        sel = np.nonzero(expert_of == e)[0]
-        ref[sel] = gemm.block_gemm(ra[sel], rsa[sel], qe, se)
-    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"{rows.size} sampled rows")
+    for e, code_hash, scale_hash, ref_rows in results:
+        assert hashlib.sha256(qb[e].cpu().numpy().tobytes()).hexdigest() == code_hash, f"expert {e} codes"
+        assert hashlib.sha256(sb[e].cpu().numpy().tobytes()).hexdigest() == scale_hash, f"expert {e} scales"
+        ref[[pos[r] for r in seg_rows[e]]] = ref_rows
+    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"first/last/inner rows of all {len(jobs)} segments")
     say("  FP8 dispatch by index: quantise the 8192 tokens, gather rows inside the GEMM")
     qt, st = fp8.fp8_quant_act_1x128(tokens.cuda())
     idx = perm.to(torch.int32).cuda()
