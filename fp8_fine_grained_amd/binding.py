@@ -38,13 +38,18 @@ _SIGS = {
                              _c.c_void_p, _c.c_int, _c.c_void_p],
     "fp8_quant_weight_128x128_dual": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
-    "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+    "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
                        _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
+    "fp8_block_gemm_accum": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
+                             _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8_block_gemm_quant": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
                              _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8_block_grouped_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
-                               _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64,
+                               _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64,
                                _c.c_int64, _c.c_int64, _c.c_void_p],
+    "fp8_block_grouped_gemm_accum": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p,
+                                     _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int, _c.c_int64,
+                                     _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8_block_grouped_gemm_gather": [_c.c_void_p, _c.c_void_p, _c.c_int64, _c.c_void_p, _c.c_void_p,
                                       _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p, _c.c_int,
                                       _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
@@ -223,9 +228,14 @@ def fp8_block_gemm(a, sa, b, sb, b_scale_mode="block", accum=None, out_dtype=tor
     _on_gpu(y)
     _contig(a, sa, b, sb, y)
     mode = {"block": B_BLOCK_128x128, "row": B_ROW_1x128}[b_scale_mode]
-    st = lib().fp8_block_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), mode, _accum_code(accum, y.dtype),
-                              _ptr(y), _dtype_code(y.dtype), M, N, K, _stream(stream))
-    _check("fp8_block_gemm", st)
+    if accum is None:  # the library's default summation for the output type
+        st = lib().fp8_block_gemm(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), mode, _ptr(y), _dtype_code(y.dtype),
+                                  M, N, K, _stream(stream))
+        _check("fp8_block_gemm", st)
+    else:
+        st = lib().fp8_block_gemm_accum(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), mode, _accum_code(accum, y.dtype),
+                                        _ptr(y), _dtype_code(y.dtype), M, N, K, _stream(stream))
+        _check("fp8_block_gemm_accum", st)
     return y
 
 
@@ -259,10 +269,15 @@ def fp8_block_grouped_gemm(a, sa, offsets, b, sb, accum=None, out_dtype=torch.bf
         y = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _on_gpu(y)
     _contig(a, sa, offsets, b, sb, y)
-    st = lib().fp8_block_grouped_gemm(_ptr(a), _ptr(sa), _ptr(offsets), G, _ptr(b), _ptr(sb),
-                                      _accum_code(accum, y.dtype), _ptr(y), _dtype_code(y.dtype),
-                                      M, N, K, _stream(stream))
-    _check("fp8_block_grouped_gemm", st)
+    if accum is None:  # the library's default summation for the output type
+        st = lib().fp8_block_grouped_gemm(_ptr(a), _ptr(sa), _ptr(offsets), G, _ptr(b), _ptr(sb), _ptr(y),
+                                          _dtype_code(y.dtype), M, N, K, _stream(stream))
+        _check("fp8_block_grouped_gemm", st)
+    else:
+        st = lib().fp8_block_grouped_gemm_accum(_ptr(a), _ptr(sa), _ptr(offsets), G, _ptr(b), _ptr(sb),
+                                                _accum_code(accum, y.dtype), _ptr(y), _dtype_code(y.dtype),
+                                                M, N, K, _stream(stream))
+        _check("fp8_block_grouped_gemm_accum", st)
     return y
 
 

@@ -152,6 +152,11 @@ int check_gemm_common(const uint8_t* a, const float* sa, const uint8_t* b, const
   return FP8FG_OK;
 }
 
+// Accumulation of the entry points without an `accum` argument: FP32 outputs
+// take exact products (the FP32 agreement they are held to), bf16 outputs the
+// full-rate FP8 matrix cores.
+int default_accum(int y_dtype) { return y_dtype == FP8FG_F32 ? FP8FG_ACCUM_EXACT : FP8FG_ACCUM_FP8_MFMA; }
+
 fp8fg::GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, void* y,
                           const int32_t* offsets, int64_t M, int64_t N, int64_t K, int64_t G, bool row_scales,
                           int accum, int y_dtype) {
@@ -167,9 +172,9 @@ fp8fg::GemmArgs gemm_args(const uint8_t* a, const float* sa, const uint8_t* b, c
 
 }  // namespace
 
-int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
-                   int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
-                   int64_t K, fp8fg_stream_t stream) {
+int fp8_block_gemm_accum(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                         int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
+                         int64_t K, fp8fg_stream_t stream) {
   if (b_scale_mode != FP8FG_B_BLOCK_128x128 && b_scale_mode != FP8FG_B_ROW_1x128)
     return FP8FG_ERR_INVALID_ARG;
   const int c = check_gemm_common(a, sa, b, sb, accum, y, y_dtype, M, N, K);
@@ -181,6 +186,12 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const fl
                                       accum, y_dtype);
   if (g.scaled && (g.row_scales || !fp8fg::fp8_block_kernel_applies(g))) return FP8FG_ERR_UNSUPPORTED;
   return hip_status(fp8fg::launch_block_gemm(g, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                   int b_scale_mode, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                   fp8fg_stream_t stream) {
+  return fp8_block_gemm_accum(a, sa, b, sb, b_scale_mode, default_accum(y_dtype), y, y_dtype, M, N, K, stream);
 }
 
 int fp8_block_gemm_quant(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int accum,
@@ -203,9 +214,16 @@ int fp8_block_gemm_quant(const uint8_t* a, const float* sa, const uint8_t* b, co
 }
 
 int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* group_offsets,
-                           int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
-                           int y_dtype, int64_t M_total, int64_t N, int64_t K,
-                           fp8fg_stream_t stream) {
+                           int64_t G, const uint8_t* b, const float* sb, void* y, int y_dtype,
+                           int64_t M_total, int64_t N, int64_t K, fp8fg_stream_t stream) {
+  return fp8_block_grouped_gemm_accum(a, sa, group_offsets, G, b, sb, default_accum(y_dtype), y, y_dtype, M_total,
+                                      N, K, stream);
+}
+
+int fp8_block_grouped_gemm_accum(const uint8_t* a, const float* sa, const int32_t* group_offsets,
+                                 int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
+                                 int y_dtype, int64_t M_total, int64_t N, int64_t K,
+                                 fp8fg_stream_t stream) {
   if (G < 0) return FP8FG_ERR_INVALID_ARG;
   const int c = check_gemm_common(a, sa, b, sb, accum, y, y_dtype, M_total, N, K);
   if (c < 0 || G == 0) return c > 0 ? c : FP8FG_OK;

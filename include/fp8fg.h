@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 6
+#define FP8FG_ABI_VERSION 7
 
 /* Status codes returned by every entry point. */
 enum {
@@ -202,7 +202,7 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
  * Block-scaled FP8 GEMM  Y = deq(A) * deq(B)^T  (innerforce accumulation
  * passage; yunhecapital section 2.2.3; tonho.wtf "como funciona").
  * For every 128-element K block kb the FP8 partial P_kb[m,n] is formed on the
- * matrix cores (summed as selected by `accum`), then promoted:
+ * matrix cores, then promoted:
  *     acc[m,n] += P_kb[m,n] * sa[m,kb] * sb(n,kb)      (FP32)
  * with sb(n,kb) = sb[n/128, kb] (FP8FG_B_BLOCK_128x128) or sb[n, kb]
  * (FP8FG_B_ROW_1x128).  Y is acc rounded to `y_dtype` (bf16: round to nearest
@@ -222,10 +222,23 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
  * accuracy is unchanged, but the order of those additions, and so the last
  * bits of those tiles, can vary from run to run.  Smaller problems and bf16
  * outputs are computed in a fixed order.
+ * The partials are summed as FP8FG_ACCUM_EXACT for FP8FG_F32 output (so FP32
+ * outputs agree with the exact result to FP32 accuracy) and as
+ * FP8FG_ACCUM_FP8_MFMA for FP8FG_BF16 output; fp8_block_gemm_accum chooses.
  */
 int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
-                   int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
-                   int64_t K, fp8fg_stream_t stream);
+                   int b_scale_mode, void* y, int y_dtype, int64_t M, int64_t N, int64_t K,
+                   fp8fg_stream_t stream);
+
+/*
+ * fp8_block_gemm with the summation of the FP8 partials chosen by `accum`
+ * (FP8FG_ACCUM_FP8_MFMA, FP8FG_ACCUM_EXACT or FP8FG_ACCUM_SCALED_MFMA; the
+ * last requires FP8FG_B_BLOCK_128x128 and N % 256 == 0).  Other arguments,
+ * requirements and behaviour as fp8_block_gemm.
+ */
+int fp8_block_gemm_accum(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb,
+                         int b_scale_mode, int accum, void* y, int y_dtype, int64_t M, int64_t N,
+                         int64_t K, fp8fg_stream_t stream);
 
 /*
  * The same GEMM with its output cast straight to FP8 for the next layer: the
@@ -237,7 +250,7 @@ int fp8_block_gemm(const uint8_t* a, const float* sa, const uint8_t* b, const fl
  * fp8_quant_act_1x128_pow2 (pow2 == 1), inside the GEMM's epilogue, so Y never
  * goes to HBM in high precision.
  *
- * a, sa, b, sb, accum, M, N, K   as fp8_block_gemm with FP8FG_B_BLOCK_128x128;
+ * a, sa, b, sb, accum, M, N, K   as fp8_block_gemm_accum with FP8FG_B_BLOCK_128x128;
  *           accum FP8FG_ACCUM_FP8_MFMA or FP8FG_ACCUM_SCALED_MFMA
  *           (FP8FG_ACCUM_EXACT: FP8FG_ERR_UNSUPPORTED).
  * q_y     out, uint8 E4M3 codes [M, N] row-major (16-byte aligned).
@@ -265,12 +278,20 @@ int fp8_block_gemm_quant(const uint8_t* a, const float* sa, const uint8_t* b, co
  * b              uint8 E4M3 [G, N, K];  sb fp32 [G, N/128, K/128] (128x128)
  * y              out, [M_total, N] of y_dtype
  * Requires K % 128 == 0, N % 128 == 0; alignment as fp8_block_gemm.
- * M_total == 0 or G == 0 is a no-op.
+ * M_total == 0 or G == 0 is a no-op.  Partials are summed as in
+ * fp8_block_gemm (exact for FP8FG_F32 output, FP8 matrix cores for
+ * FP8FG_BF16); fp8_block_grouped_gemm_accum chooses.
  */
 int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* group_offsets,
-                           int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
-                           int y_dtype, int64_t M_total, int64_t N, int64_t K,
-                           fp8fg_stream_t stream);
+                           int64_t G, const uint8_t* b, const float* sb, void* y, int y_dtype,
+                           int64_t M_total, int64_t N, int64_t K, fp8fg_stream_t stream);
+
+/* fp8_block_grouped_gemm with the summation chosen by `accum` (as
+ * fp8_block_gemm_accum; FP8FG_ACCUM_SCALED_MFMA requires N % 256 == 0). */
+int fp8_block_grouped_gemm_accum(const uint8_t* a, const float* sa, const int32_t* group_offsets,
+                                 int64_t G, const uint8_t* b, const float* sb, int accum, void* y,
+                                 int y_dtype, int64_t M_total, int64_t N, int64_t K,
+                                 fp8fg_stream_t stream);
 
 /*
  * The grouped GEMM reading its rows through an index: FP8 dispatch without a
@@ -284,7 +305,7 @@ int fp8_block_grouped_gemm(const uint8_t* a, const float* sa, const int32_t* gro
  * row_index  DEVICE int32 [M_total], values in [0, T) (values outside are
  *            clamped into it: unspecified rows, never an access outside a_tok)
  * group_offsets, G, b, sb, accum, y, y_dtype, M_total, N, K
- *            as fp8_block_grouped_gemm (y stays in routed-row order).
+ *            as fp8_block_grouped_gemm_accum (y stays in routed-row order).
  * Requires N % 256 == 0, K % 128 == 0, T * K < 2^32 (32-bit row offsets),
  * T >= 1 when M_total > 0; row_index 4-byte aligned; other alignment as
  * fp8_block_gemm.  M_total == 0 or G == 0 is a no-op.

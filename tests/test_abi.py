@@ -22,14 +22,15 @@ def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
                           "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual", "fp8_quant_per_tensor",
-                          "fp8_block_gemm", "fp8_block_gemm_quant", "fp8_block_grouped_gemm", "fp8_block_grouped_gemm_gather",
+                          "fp8_block_gemm", "fp8_block_gemm_accum", "fp8_block_gemm_quant", "fp8_block_grouped_gemm",
+                          "fp8_block_grouped_gemm_accum", "fp8_block_grouped_gemm_gather",
                           "fp8fg_status_string", "fp8fg_abi_version"}
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 6
+    assert L.fp8fg_abi_version() == 7
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -96,8 +97,27 @@ def test_quant_weight_dual_validation(L):
     assert f(*args(ld=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
 
 
+def test_survey_signatures_take_no_accumulation_argument(L):
+    """fp8_block_gemm and fp8_block_grouped_gemm have the boundary's argument
+    lists; their validation matches the *_accum forms with the default mode."""
+    g = L.fp8_block_gemm
+    assert len(g.argtypes) == 11
+    base = [GOOD, GOOD, GOOD, GOOD, fp8.B_BLOCK_128x128, GOOD, fp8.BF16, 4, 128, 256, NULL]
+    assert g(*[5 if i == 4 else v for i, v in enumerate(base)]) == fp8.ERR_INVALID_ARG
+    assert g(*[200 if i == 9 else v for i, v in enumerate(base)]) == fp8.ERR_UNSUPPORTED
+    assert g(*[BAD if i == 5 else v for i, v in enumerate(base)]) == fp8.ERR_MISALIGNED
+    assert g(*[NULL if i == 0 else (0 if i == 7 else v) for i, v in enumerate(base)]) == fp8.OK
+    h = L.fp8_block_grouped_gemm
+    assert len(h.argtypes) == 12
+    gb = [GOOD, GOOD, GOOD, 4, GOOD, GOOD, GOOD, fp8.BF16, 64, 128, 256, NULL]
+    assert h(*[-1 if i == 3 else v for i, v in enumerate(gb)]) == fp8.ERR_INVALID_ARG
+    assert h(*[NULL if i == 2 else v for i, v in enumerate(gb)]) == fp8.ERR_INVALID_ARG
+    assert h(*[192 if i == 9 else v for i, v in enumerate(gb)]) == fp8.ERR_UNSUPPORTED
+    assert h(*[0 if i == 3 else v for i, v in enumerate(gb)]) == fp8.OK
+
+
 def test_gemm_validation(L):
-    f = L.fp8_block_gemm
+    f = L.fp8_block_gemm_accum
     args = lambda **kw: [kw.get(k, v) for k, v in (
         ("a", GOOD), ("sa", GOOD), ("b", GOOD), ("sb", GOOD), ("mode", fp8.B_BLOCK_128x128),
         ("accum", fp8.ACCUM_FP8_MFMA), ("y", GOOD), ("ydt", fp8.BF16), ("M", 4), ("N", 128),
@@ -120,7 +140,7 @@ def test_gemm_validation(L):
 
 
 def test_grouped_validation(L):
-    f = L.fp8_block_grouped_gemm
+    f = L.fp8_block_grouped_gemm_accum
     args = lambda **kw: [kw.get(k, v) for k, v in (
         ("a", GOOD), ("sa", GOOD), ("off", GOOD), ("G", 4), ("b", GOOD), ("sb", GOOD),
         ("accum", fp8.ACCUM_FP8_MFMA), ("y", GOOD), ("ydt", fp8.BF16), ("M", 64), ("N", 128),
