@@ -32,6 +32,17 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 
 
+// Codes are written with ordinary (cache-allocating) stores, inputs read with
+// non-temporal loads: the GEMM that follows reads the codes, and stores that
+// allocate keep them (X 29 MB + W 51 MB for the dense projection) in the 256 MB
+// last-level cache, while the streamed bf16 inputs, read once, do not displace
+// them.  Measured on the dense step against non-temporal code stores: GEMM 201
+// -> 194 us, quantisers unchanged.
+template <typename V>
+__device__ __forceinline__ void store_codes(const V& v, void* p) {
+  *reinterpret_cast<V*>(p) = v;
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
@@ -112,7 +123,7 @@ __global__ void __launch_bounds__(256) quant_act_rows_kernel(const void* __restr
   out.z = cvt4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
   out.w = cvt4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
   if (live) {
-    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(q + m * K + col));
+    store_codes(out, reinterpret_cast<u32x4*>(q + m * K + col));
     if (part == 0) scales[t] = s;
   }
 }
@@ -188,7 +199,7 @@ __global__ void __launch_bounds__(256) quant_pt_cast_kernel(const void* __restri
   out.y = cvt4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
   out.z = cvt4(v[8] * inv, v[9] * inv, v[10] * inv, v[11] * inv);
   out.w = cvt4(v[12] * inv, v[13] * inv, v[14] * inv, v[15] * inv);
-  __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(q + m * K + col));
+  store_codes(out, reinterpret_cast<u32x4*>(q + m * K + col));
   if (part == 0 && tile >= 1 && tile < n_scales) scales[tile] = s;
 }
 
@@ -281,7 +292,7 @@ __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restr
   o.y = cvt4(lo(w[4]) * inv0, lo(w[5]) * inv0, lo(w[6]) * inv0, lo(w[7]) * inv0);
   o.z = cvt4(lo(w[8]) * inv0, lo(w[9]) * inv0, lo(w[10]) * inv0, lo(w[11]) * inv0);
   o.w = cvt4(lo(w[12]) * inv0, lo(w[13]) * inv0, lo(w[14]) * inv0, lo(w[15]) * inv0);
-  __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(q + m0 * K + k0));
+  store_codes(o, reinterpret_cast<u32x4*>(q + m0 * K + k0));
   if (tg == 0) scales[m0 * G + g] = s0;
   if constexpr (BF16) {
     float s1, inv1;
@@ -291,7 +302,7 @@ __global__ void __launch_bounds__(512) quant_act_cols_kernel(const void* __restr
     h.y = cvt4(bf16_hi(w[4]) * inv1, bf16_hi(w[5]) * inv1, bf16_hi(w[6]) * inv1, bf16_hi(w[7]) * inv1);
     h.z = cvt4(bf16_hi(w[8]) * inv1, bf16_hi(w[9]) * inv1, bf16_hi(w[10]) * inv1, bf16_hi(w[11]) * inv1);
     h.w = cvt4(bf16_hi(w[12]) * inv1, bf16_hi(w[13]) * inv1, bf16_hi(w[14]) * inv1, bf16_hi(w[15]) * inv1);
-    __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(q + (m0 + 1) * K + k0));
+    store_codes(h, reinterpret_cast<u32x4*>(q + (m0 + 1) * K + k0));
     if (tg == 0) scales[(m0 + 1) * G + g] = s1;
   }
 }
@@ -346,7 +357,7 @@ __global__ void __launch_bounds__(256) quant_weight_kernel(const void* __restric
     u32x2 o;
     o.x = cvt4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
     o.y = cvt4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
-    __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(q + row * K + static_cast<int64_t>(bj) * 128 + c8));
+    store_codes(o, reinterpret_cast<u32x2*>(q + row * K + static_cast<int64_t>(bj) * 128 + c8));
   }
   if (threadIdx.x == 0) scales[blockIdx.x] = s;
 }
@@ -426,7 +437,7 @@ __global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __re
 #pragma unroll
     for (int d = 0; d < 4; ++d)
       codes[rr][d] = cvt4(v[rr][4 * d] * inv, v[rr][4 * d + 1] * inv, v[rr][4 * d + 2] * inv, v[rr][4 * d + 3] * inv);
-    __builtin_nontemporal_store(u32x4{codes[rr][0], codes[rr][1], codes[rr][2], codes[rr][3]},
+    store_codes(u32x4{codes[rr][0], codes[rr][1], codes[rr][2], codes[rr][3]},
                                 reinterpret_cast<u32x4*>(q + row * K + static_cast<int64_t>(bj) * 128 + cg * 16));
   }
   // Transposed tile: row c = column of the block (a K index), dword q4 = its 4
@@ -448,7 +459,7 @@ __global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __re
     const int idx = threadIdx.x + 256 * t;
     const int c = idx >> 3, ch = idx & 7;
     const u32x4 val = *reinterpret_cast<const u32x4*>(&tr[c * 32 + 4 * (ch ^ (((c >> 4) & 3) << 1))]);
-    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(qt + (static_cast<int64_t>(bj) * 128 + c) * N +
+    store_codes(val, reinterpret_cast<u32x4*>(qt + (static_cast<int64_t>(bj) * 128 + c) * N +
                                                               static_cast<int64_t>(bi) * 128 + ch * 16));
   }
   if (threadIdx.x == 0) {
