@@ -74,18 +74,21 @@ def stats(csv_path, out_md, command, bench_log=None):
     bench = _bench_line(bench_log) if bench_log else None
     trace = os.path.join(os.path.dirname(csv_path), os.path.basename(csv_path).replace("kernel_stats", "kernel_trace"))
     if bench and os.path.exists(trace):
-        # the timed launches are each kernel's last `steps` dispatches
+        # The timed launches are the last `steps` dispatches of each kernel and
+        # launch shape (grid size): the bench's extra lines after the step (the
+        # same quantisers on other shapes) have grids of their own.
         n = int(bench["steps"])
         durs = {}
         for r in _rows(trace):
-            durs.setdefault(r["Kernel_Name"], []).append(
+            durs.setdefault((r["Kernel_Name"], int(r["Grid_Size_X"])), []).append(
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-        lines += ["", f"rocprofv3 average over each kernel's last {n} dispatches (the timed steps):", "",
-                  "| kernel | dispatches | average (us) |", "|---|---|---|"]
-        for name, d in durs.items():
+        lines += ["", f"rocprofv3 average over the last {n} dispatches of each kernel and grid size (the timed",
+                  "steps, and the last launches of each extra line):", "",
+                  "| kernel | grid (threads) | dispatches | average (us) |", "|---|---|---|---|"]
+        for (name, grid), d in durs.items():
             d = [x for _, x in sorted(d)][-n:]
             short = name if len(name) <= 110 else name[:107] + "..."
-            lines.append(f"| `{short}` | {len(d)} | {sum(d) / len(d) / 1e3:.2f} |")
+            lines.append(f"| `{short}` | {grid} | {len(d)} | {sum(d) / len(d) / 1e3:.2f} |")
     if bench:
         lines += ["", "bench.py's own HIP-event averages over the same timed steps (the first table also",
                   "counts the warm-up launches):", "", "| launch | ms |", "|---|---|"]
