@@ -49,7 +49,11 @@
 //    contiguous band of the tile grid, keeping its operand panels in its L2;
 //    grouped tiles are in expert-major order, so one XCD works through one
 //    expert's tiles at a time.
+//  * Grouped tiles multiply only the 16-row sub-tiles that hold rows of the
+//    expert's segment: the K loop is compiled for 1 .. SM row sub-tiles and a
+//    wavefront runs the copy for its live rows, chosen once per tile.
 #include <atomic>
+#include <type_traits>
 
 #include "launch.h"
 #include "quant_rule.h"
@@ -529,7 +533,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     dma_scale(kb, st);
   };
 
-  v4f acc[SN][SM];
+  v4f acc[SN][SM];  // (a wavefront with fewer live row sub-tiles uses the first SMW columns)
 #pragma unroll
   for (int i = 0; i < SN; ++i)
 #pragma unroll
@@ -569,319 +573,349 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
   // matrix) has no product to form: it only issues its share of the tile loads
   // and meets the barriers, so the SIMD it shares runs the other wavefront's
   // MFMAs alone.
-  const bool wave_live = __builtin_amdgcn_readfirstlane(static_cast<int>(row_lo + wm * TM < row_hi)) != 0;
-  if (!wave_live) {
-    int st = 0;
+  // The wavefront's part of the tile: SMW row sub-tiles from tile row roff
+  // (SMW = SM except for grouped tiles, below).
+  auto body = [&](auto smc, const int roff) {
+    constexpr int SMW = decltype(smc)::value;
+    constexpr int TMW = SMW * 16;
+    const bool wave_live = __builtin_amdgcn_readfirstlane(static_cast<int>(row_lo + roff < row_hi)) != 0;
+    if (!wave_live) {
+      int st = 0;
+      for (int kb = 0; kb < KB; ++kb) {
+        const int st_fill = st == 0 ? STAGES - 1 : st - 1;
+        const int kb_fill = clampkb(kb + STAGES - 1);
+  #pragma unroll
+        for (int d = 0; d < ND; ++d) dma_tile(d, kb_fill, st_fill);
+        if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
+        prefetch(clampkb(kb + PF));
+        wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
+        st = st == STAGES - 1 ? 0 : st + 1;
+      }
+    } else {
+    v8i fm[SMW];
+    float f[SMW];
+    // Grouped tiles read each n fragment two sub-tile steps ahead (fn1 holds the
+    // next one): 2% faster on the MoE shape, where a step is 4 MFMAs; the dense
+    // tiles read one step ahead (two ahead measured 1.5% slower with eight
+    // wavefronts and 18% slower with four).
+    constexpr bool FD2 = GROUPED && SN > 2;
+    v8i fn, fn1;
+    // Scaled mode: E8M0 codes (the fp32 exponent field) of the lane's act-row
+    // scale in each m sub-tile, and of the wavefront's weight-block scale.
+    int ex[SMW];
+    int ew = 0;
+    auto e8m0 = [](float v) { return static_cast<int>((__float_as_uint(v) >> 23) & 0xFFu); };
+    auto act_scale = [&](int st, int j) { return s_sa[st][roff + j * 16 + (lane & 15)]; };
+    auto wgt_scale = [&](int st) { return s_sb[st][((wn * TN) / 128) % SB_LEN]; };
+    // acc += 2^(ew-127) * 2^(ex-127) * (128-K FP8 partial), in one instruction; MFMA
+    // "A" is the weight fragment (scale per weight row), "B" the act fragment.
+    auto mma_scaled = [](const v8i& wfrag, const v8i& afrag, const v4f& c, int ewv, int exv) {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfrag, afrag, c, 0, 0, 0, ewv, 0, exv);
+    };
+    auto factor = [&](int st, int j) {
+      const float a = s_sa[st][roff + j * 16 + (lane & 15)];
+      if constexpr (ROWS || !BALIGN)
+        return a;
+      else
+        return a * s_sb[st][(wn * TN) / 128];
+    };
+    // Unaligned weight tiles: the block scale of n sub-tile i (staged blocks start
+    // at block n0/128).
+    const int n0_in_blk = static_cast<int>(n0 % 128);
+    auto sub_scale = [&](int st, int i) { return s_sb[st][((n0_in_blk + wn * TN + i * 16) / 128) % SB_LEN]; };
+    float sbv[BALIGN ? 1 : SN];
+    // Row mode: the 4 weight-row scales of this lane in n sub-tile i.
+    auto row_scales = [&](int st, int i) {
+      return *reinterpret_cast<const v4f*>(&s_sb[st][(wn * TN + i * 16 + 4 * (lane >> 4)) % SB_LEN]);
+    };
+    {
+      const uint8_t* tA = tiles;
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j) {
+        fm[j] = frag(tA, roff + j * 16, lane);
+        if constexpr (SCALED)
+          ex[j] = e8m0(act_scale(0, j));
+        else
+          f[j] = factor(0, j);
+      }
+      if constexpr (SCALED) ew = e8m0(wgt_scale(0));
+      fn = frag(tA + TILE_A, wn * TN, lane);
+      if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
+    }
+
+    // 128-K partial of n sub-tile `b` and m sub-tile `a` (MFMA A = weight rows).
+    WideFrag wm_frag[EXACT ? SMW : 1];
+    auto partial = [&](const v8i& b, const WideFrag& wb, int j) {
+      const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (!EXACT) {
+        (void)wb;
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, fm[j], z, 0, 0, 0, 0, 0, 0);
+      } else {
+        (void)b;
+        v4f r = z;
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) r = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb.q[q], wm_frag[j].q[q], r, 0, 0, 0);
+        return r;
+      }
+    };
+    // acc[i] += P * factor, with the row scales of sub-tile i in row mode, or the
+    // block scale bs of sub-tile i for unaligned weight tiles.
+    auto promote = [&](v4f* a, const v4f (&P)[SMW], const float (&fv)[SMW], const v4f& sbr, float bs) {
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j) {
+        const float fj = BALIGN ? fv[j] : fv[j] * bs;
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (ROWS)
+            a[j][r] = fmaf(P[j][r] * sbr[r], fv[j], a[j][r]);
+          else
+            a[j][r] = fmaf(P[j][r], fj, a[j][r]);
+        }
+      }
+    };
+    auto bsv = [&](int i) { if constexpr (BALIGN) return 0.0f; else return sbv[i]; };
+
+    int st = 0;  // stage holding block kb
+    v4f P[2][SMW];
+    v4f sbr[2];  // row mode: row scales of the sub-tiles whose partials are pending
+    // Grouped tiles: the last sub-tile's partials are formed right after the
+    // barrier; promoting them at once would wait on those MFMAs (s_nop hazards).
+    // Their promotion is deferred to the first sub-tile step of the next block,
+    // with the block's factors kept in f_prev (P[(SN-1)&1] and sbr[(SN-1)&1] are
+    // not rewritten before then: step 0 writes the other buffer).  1.8% faster on
+    // the MoE shape; 1% slower on the dense 256 x 256 tile, which keeps the
+    // immediate promotion.
+    constexpr bool DEFER = GROUPED && !SCALED && BALIGN;
+    static_assert(!DEFER || SN % 2 == 0, "the deferred partials use the buffer step 0 does not write");
+    float f_prev[SMW];
     for (int kb = 0; kb < KB; ++kb) {
+      // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
+      // Near the end the free stage is refilled with block KB-1, which is not read
+      // again: the loop body stays branch-free and every wait is the same.
       const int st_fill = st == 0 ? STAGES - 1 : st - 1;
       const int kb_fill = clampkb(kb + STAGES - 1);
-#pragma unroll
-      for (int d = 0; d < ND; ++d) dma_tile(d, kb_fill, st_fill);
-      if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
-      prefetch(clampkb(kb + PF));
+      const uint8_t* tB = tiles + st * STAGE + TILE_A;
+      if constexpr (!BALIGN) {
+  #pragma unroll
+        for (int i = 0; i < SN; ++i) sbv[i] = sub_scale(st, i);
+      }
+      if constexpr (EXACT) {
+  #pragma unroll
+        for (int j = 0; j < SMW; ++j) wm_frag[j] = widen(fm[j]);
+      }
+      __builtin_amdgcn_s_setprio(1);  // the issuing phase of the matrix cores goes first
+      // Sub-tile steps 0 .. SN-2: the fragment of step i+1 is read from LDS while
+      // the MFMAs of step i run, and the promotion FMAs of step i-1 (double-
+      // buffered partials) fill the VALU under them.
+  #pragma unroll
+      for (int i = 0; i < SN - 1; ++i) {
+        // The loads of the block being prefetched go out over the first SPREAD
+        // sub-tile steps, between MFMAs.
+        if (i < SPREAD) {
+  #pragma unroll
+          for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
+        }
+        if (i == 0) {
+          // With two stages every wait drains all loads, so the filler DMAs that
+          // keep the per-wavefront load count uniform are only needed with more.
+          if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
+        }
+        if (i == SN - 2) prefetch(clampkb(kb + PF));  // after this iteration's DMAs
+        v8i fn_next;  // the fragment this step reads: step i + 1's, or i + 2's with FD2
+        if constexpr (FD2) {
+          if (i + 2 < SN) fn_next = frag(tB, wn * TN + (i + 2) * 16, lane);
+        } else {
+          fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
+        }
+        if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
+        if constexpr (SCALED) {
+          const int ewi = BALIGN ? ew : e8m0(bsv(i));
+  #pragma unroll
+          for (int j = 0; j < SMW; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
+        } else {
+          WideFrag wn_frag;
+          if constexpr (EXACT) wn_frag = widen(fn);
+  #pragma unroll
+          for (int j = 0; j < SMW; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
+          if (i > 0)
+            promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
+          else if (DEFER && kb > 0)
+            promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
+        }
+        if constexpr (FD2) {
+          fn = fn1;
+          if (i + 2 < SN) fn1 = fn_next;
+        } else {
+          fn = fn_next;
+        }
+      }
+      if constexpr (ROWS) sbr[(SN - 1) & 1] = row_scales(st, SN - 1);
+
+      // Every LDS read of this stage has been issued: once they have returned and
+      // block kb+1 is resident, the workgroup synchronises.  The last step's MFMAs
+      // run after the barrier, and the next block's fragments are requested as
+      // each m fragment is consumed, so their LDS latency hides under the MFMAs.
+      __builtin_amdgcn_s_setprio(0);
+      // the newest load, this iteration's prefetch, may stay in flight
       wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
       st = st == STAGES - 1 ? 0 : st + 1;
-    }
-  } else {
-  v8i fm[SM];
-  float f[SM];
-  // Grouped tiles read each n fragment two sub-tile steps ahead (fn1 holds the
-  // next one): 2% faster on the MoE shape, where a step is 4 MFMAs; the dense
-  // tiles read one step ahead (two ahead measured 1.5% slower with eight
-  // wavefronts and 18% slower with four).
-  constexpr bool FD2 = GROUPED && SN > 2;
-  v8i fn, fn1;
-  // Scaled mode: E8M0 codes (the fp32 exponent field) of the lane's act-row
-  // scale in each m sub-tile, and of the wavefront's weight-block scale.
-  int ex[SM];
-  int ew = 0;
-  auto e8m0 = [](float v) { return static_cast<int>((__float_as_uint(v) >> 23) & 0xFFu); };
-  auto act_scale = [&](int st, int j) { return s_sa[st][wm * TM + j * 16 + (lane & 15)]; };
-  auto wgt_scale = [&](int st) { return s_sb[st][((wn * TN) / 128) % SB_LEN]; };
-  // acc += 2^(ew-127) * 2^(ex-127) * (128-K FP8 partial), in one instruction; MFMA
-  // "A" is the weight fragment (scale per weight row), "B" the act fragment.
-  auto mma_scaled = [](const v8i& wfrag, const v8i& afrag, const v4f& c, int ewv, int exv) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfrag, afrag, c, 0, 0, 0, ewv, 0, exv);
-  };
-  auto factor = [&](int st, int j) {
-    const float a = s_sa[st][wm * TM + j * 16 + (lane & 15)];
-    if constexpr (ROWS || !BALIGN)
-      return a;
-    else
-      return a * s_sb[st][(wn * TN) / 128];
-  };
-  // Unaligned weight tiles: the block scale of n sub-tile i (staged blocks start
-  // at block n0/128).
-  const int n0_in_blk = static_cast<int>(n0 % 128);
-  auto sub_scale = [&](int st, int i) { return s_sb[st][((n0_in_blk + wn * TN + i * 16) / 128) % SB_LEN]; };
-  float sbv[BALIGN ? 1 : SN];
-  // Row mode: the 4 weight-row scales of this lane in n sub-tile i.
-  auto row_scales = [&](int st, int i) {
-    return *reinterpret_cast<const v4f*>(&s_sb[st][(wn * TN + i * 16 + 4 * (lane >> 4)) % SB_LEN]);
-  };
-  {
-    const uint8_t* tA = tiles;
-#pragma unroll
-    for (int j = 0; j < SM; ++j) {
-      fm[j] = frag(tA, wm * TM + j * 16, lane);
-      if constexpr (SCALED)
-        ex[j] = e8m0(act_scale(0, j));
-      else
-        f[j] = factor(0, j);
-    }
-    if constexpr (SCALED) ew = e8m0(wgt_scale(0));
-    fn = frag(tA + TILE_A, wn * TN, lane);
-    if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
-  }
-
-  // 128-K partial of n sub-tile `b` and m sub-tile `a` (MFMA A = weight rows).
-  WideFrag wm_frag[EXACT ? SM : 1];
-  auto partial = [&](const v8i& b, const WideFrag& wb, int j) {
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (!EXACT) {
-      (void)wb;
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, fm[j], z, 0, 0, 0, 0, 0, 0);
-    } else {
-      (void)b;
-      v4f r = z;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) r = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb.q[q], wm_frag[j].q[q], r, 0, 0, 0);
-      return r;
-    }
-  };
-  // acc[i] += P * factor, with the row scales of sub-tile i in row mode, or the
-  // block scale bs of sub-tile i for unaligned weight tiles.
-  auto promote = [&](v4f (&a)[SM], const v4f (&P)[SM], const float (&fv)[SM], const v4f& sbr, float bs) {
-#pragma unroll
-    for (int j = 0; j < SM; ++j) {
-      const float fj = BALIGN ? fv[j] : fv[j] * bs;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (ROWS)
-          a[j][r] = fmaf(P[j][r] * sbr[r], fv[j], a[j][r]);
-        else
-          a[j][r] = fmaf(P[j][r], fj, a[j][r]);
-      }
-    }
-  };
-  auto bsv = [&](int i) { if constexpr (BALIGN) return 0.0f; else return sbv[i]; };
-
-  int st = 0;  // stage holding block kb
-  v4f P[2][SM];
-  v4f sbr[2];  // row mode: row scales of the sub-tiles whose partials are pending
-  // Grouped tiles: the last sub-tile's partials are formed right after the
-  // barrier; promoting them at once would wait on those MFMAs (s_nop hazards).
-  // Their promotion is deferred to the first sub-tile step of the next block,
-  // with the block's factors kept in f_prev (P[(SN-1)&1] and sbr[(SN-1)&1] are
-  // not rewritten before then: step 0 writes the other buffer).  1.8% faster on
-  // the MoE shape; 1% slower on the dense 256 x 256 tile, which keeps the
-  // immediate promotion.
-  constexpr bool DEFER = GROUPED && !SCALED && BALIGN;
-  static_assert(!DEFER || SN % 2 == 0, "the deferred partials use the buffer step 0 does not write");
-  float f_prev[SM];
-  for (int kb = 0; kb < KB; ++kb) {
-    // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
-    // Near the end the free stage is refilled with block KB-1, which is not read
-    // again: the loop body stays branch-free and every wait is the same.
-    const int st_fill = st == 0 ? STAGES - 1 : st - 1;
-    const int kb_fill = clampkb(kb + STAGES - 1);
-    const uint8_t* tB = tiles + st * STAGE + TILE_A;
-    if constexpr (!BALIGN) {
-#pragma unroll
-      for (int i = 0; i < SN; ++i) sbv[i] = sub_scale(st, i);
-    }
-    if constexpr (EXACT) {
-#pragma unroll
-      for (int j = 0; j < SM; ++j) wm_frag[j] = widen(fm[j]);
-    }
-    __builtin_amdgcn_s_setprio(1);  // the issuing phase of the matrix cores goes first
-    // Sub-tile steps 0 .. SN-2: the fragment of step i+1 is read from LDS while
-    // the MFMAs of step i run, and the promotion FMAs of step i-1 (double-
-    // buffered partials) fill the VALU under them.
-#pragma unroll
-    for (int i = 0; i < SN - 1; ++i) {
-      // The loads of the block being prefetched go out over the first SPREAD
-      // sub-tile steps, between MFMAs.
-      if (i < SPREAD) {
-#pragma unroll
-        for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
-      }
-      if (i == 0) {
-        // With two stages every wait drains all loads, so the filler DMAs that
-        // keep the per-wavefront load count uniform are only needed with more.
-        if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
-      }
-      if (i == SN - 2) prefetch(clampkb(kb + PF));  // after this iteration's DMAs
-      v8i fn_next;  // the fragment this step reads: step i + 1's, or i + 2's with FD2
-      if constexpr (FD2) {
-        if (i + 2 < SN) fn_next = frag(tB, wn * TN + (i + 2) * 16, lane);
-      } else {
-        fn_next = frag(tB, wn * TN + (i + 1) * 16, lane);
-      }
-      if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
       if constexpr (SCALED) {
-        const int ewi = BALIGN ? ew : e8m0(bsv(i));
-#pragma unroll
-        for (int j = 0; j < SM; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
-      } else {
+        const uint8_t* tA = tiles + st * STAGE;
+        const int ew_old = BALIGN ? ew : e8m0(bsv(SN - 1));
+  #pragma unroll
+        for (int j = 0; j < SMW; ++j) {
+          acc[SN - 1][j] = mma_scaled(fn, fm[j], acc[SN - 1][j], ew_old, ex[j]);
+          // (After the final block this reads a stage nobody uses; the values are dropped.)
+          fm[j] = frag(tA, roff + j * 16, lane);
+          ex[j] = e8m0(act_scale(st, j));
+        }
+        ew = e8m0(wgt_scale(st));
+        fn = frag(tA + TILE_A, wn * TN, lane);
+        if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
+        continue;
+      }
+      float f_old[SMW];
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j) f_old[j] = f[j];
+      {
+        const uint8_t* tA = tiles + st * STAGE;
         WideFrag wn_frag;
         if constexpr (EXACT) wn_frag = widen(fn);
-#pragma unroll
-        for (int j = 0; j < SM; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
-        if (i > 0)
-          promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
-        else if (DEFER && kb > 0)
-          promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
+  #pragma unroll
+        for (int j = 0; j < SMW; ++j) {
+          P[(SN - 1) & 1][j] = partial(fn, wn_frag, j);
+          // (After the final block this reads a stage nobody uses; the values are dropped.)
+          fm[j] = frag(tA, roff + j * 16, lane);
+          f[j] = factor(st, j);
+        }
+        fn = frag(tA + TILE_A, wn * TN, lane);
+        if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
       }
-      if constexpr (FD2) {
-        fn = fn1;
-        if (i + 2 < SN) fn1 = fn_next;
+      promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
+      if constexpr (DEFER) {
+  #pragma unroll
+        for (int j = 0; j < SMW; ++j) f_prev[j] = f_old[j];
       } else {
-        fn = fn_next;
+        promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
       }
     }
-    if constexpr (ROWS) sbr[(SN - 1) & 1] = row_scales(st, SN - 1);
-
-    // Every LDS read of this stage has been issued: once they have returned and
-    // block kb+1 is resident, the workgroup synchronises.  The last step's MFMAs
-    // run after the barrier, and the next block's fragments are requested as
-    // each m fragment is consumed, so their LDS latency hides under the MFMAs.
-    __builtin_amdgcn_s_setprio(0);
-    // the newest load, this iteration's prefetch, may stay in flight
-    wait_barrier<WAIT_N + (PF > 0 ? 1 : 0)>();
-    st = st == STAGES - 1 ? 0 : st + 1;
-    if constexpr (SCALED) {
-      const uint8_t* tA = tiles + st * STAGE;
-      const int ew_old = BALIGN ? ew : e8m0(bsv(SN - 1));
-#pragma unroll
-      for (int j = 0; j < SM; ++j) {
-        acc[SN - 1][j] = mma_scaled(fn, fm[j], acc[SN - 1][j], ew_old, ex[j]);
-        // (After the final block this reads a stage nobody uses; the values are dropped.)
-        fm[j] = frag(tA, wm * TM + j * 16, lane);
-        ex[j] = e8m0(act_scale(st, j));
-      }
-      ew = e8m0(wgt_scale(st));
-      fn = frag(tA + TILE_A, wn * TN, lane);
-      if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
-      continue;
-    }
-    float f_old[SM];
-#pragma unroll
-    for (int j = 0; j < SM; ++j) f_old[j] = f[j];
-    {
-      const uint8_t* tA = tiles + st * STAGE;
-      WideFrag wn_frag;
-      if constexpr (EXACT) wn_frag = widen(fn);
-#pragma unroll
-      for (int j = 0; j < SM; ++j) {
-        P[(SN - 1) & 1][j] = partial(fn, wn_frag, j);
-        // (After the final block this reads a stage nobody uses; the values are dropped.)
-        fm[j] = frag(tA, wm * TM + j * 16, lane);
-        f[j] = factor(st, j);
-      }
-      fn = frag(tA + TILE_A, wn * TN, lane);
-      if constexpr (FD2) fn1 = frag(tA + TILE_A, wn * TN + 16, lane);
-    }
-    promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
     if constexpr (DEFER) {
-#pragma unroll
-      for (int j = 0; j < SM; ++j) f_prev[j] = f_old[j];
-    } else {
-      promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
+      if (KB > 0) promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
     }
-  }
-  if constexpr (DEFER) {
-    if (KB > 0) promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
-  }
-  }  // live wavefront
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
+    }  // live wavefront
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no LDS DMA may outlive the workgroup
 
-  // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
-  __syncthreads();  // every wavefront is done with the tile buffers
-  if constexpr (QOUT != 0) {
-    // The wavefront's 128 columns of a row are one 1x128 group.  Row m = j*16 +
-    // (lane & 15) of sub-tile column j sits in lanes l, l^16, l^32, l^48, 32
-    // values each: amax over the lane's values, then over those four lanes.
-    // Codes are staged in LDS as 128-byte rows and leave as whole rows.
-    constexpr int QP = 128 + 16;  // staging pitch (bytes)
-    static_assert(NW * TM * QP <= TILES_BYTES, "staging fits the tile buffers");
-    uint8_t* epi = tiles + wave * TM * QP;
-    const int64_t gcol = (n0 + wn * TN) / 128;  // group index along N
-#pragma unroll
-    for (int j = 0; j < SM; ++j) {
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < SN; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[i][j][r]));
-      am = fmaxf(am, __shfl_xor(am, 16));
-      am = fmaxf(am, __shfl_xor(am, 32));
-      float sc, inv;
-      group_scale<QOUT == 2>(am, sc, inv);
-      const int mr = j * 16 + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < SN; ++i)
-        *reinterpret_cast<uint32_t*>(epi + mr * QP + i * 16 + 4 * (lane >> 4)) =
-            cvt4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
-      const int64_t m = row_lo + wm * TM + mr;
-      if (lane < 16 && m < row_hi) p.ys[m * (p.N / 128) + gcol] = sc;
-    }
-    // (ds ops of one wavefront complete in order: no barrier needed here)
-#pragma unroll
-    for (int pass = 0; pass < TM / 8; ++pass) {
-      const int mr = pass * 8 + lane / 8;
-      const int64_t m = row_lo + wm * TM + mr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * QP + (lane % 8) * 16);
-      if (m < row_hi)
-        *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.y) + m * p.N + n0 + wn * TN + (lane % 8) * 16) = v;
-    }
-  } else if constexpr (BF16OUT) {
-    // Stage the wavefront's TM x TN block as bf16 rows in LDS (8 bytes per lane
-    // and sub-tile), then write whole row segments (TN*2 bytes = 16 lanes x 16 B).
-    uint8_t* epi = tiles + wave * TM * EPI_PITCH;
-#pragma unroll
-    for (int j = 0; j < SM; ++j)
-#pragma unroll
-      for (int i = 0; i < SN; ++i) {
+    // ---- epilogue: lane holds Y[m][n .. n+3], m = sub-tile column, n = 4 consecutive rows
+    __syncthreads();  // every wavefront is done with the tile buffers
+    if constexpr (QOUT != 0) {
+      // The wavefront's 128 columns of a row are one 1x128 group.  Row m = j*16 +
+      // (lane & 15) of sub-tile column j sits in lanes l, l^16, l^32, l^48, 32
+      // values each: amax over the lane's values, then over those four lanes.
+      // Codes are staged in LDS as 128-byte rows and leave as whole rows.
+      constexpr int QP = 128 + 16;  // staging pitch (bytes)
+      static_assert(NW * TM * QP <= TILES_BYTES, "staging fits the tile buffers");
+      uint8_t* epi = tiles + wave * TM * QP;
+      const int64_t gcol = (n0 + wn * TN) / 128;  // group index along N
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j) {
+        float am = 0.0f;
+  #pragma unroll
+        for (int i = 0; i < SN; ++i)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[i][j][r]));
+        am = fmaxf(am, __shfl_xor(am, 16));
+        am = fmaxf(am, __shfl_xor(am, 32));
+        float sc, inv;
+        group_scale<QOUT == 2>(am, sc, inv);
         const int mr = j * 16 + (lane & 15);
-        const int nc = i * 16 + 4 * (lane >> 4);
-        u32x2 o;
-        o[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        o[1] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
-        *reinterpret_cast<u32x2*>(epi + mr * EPI_PITCH + nc * 2) = o;
+  #pragma unroll
+        for (int i = 0; i < SN; ++i)
+          *reinterpret_cast<uint32_t*>(epi + mr * QP + i * 16 + 4 * (lane >> 4)) =
+              cvt4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
+        const int64_t m = row_lo + roff + mr;
+        if (lane < 16 && m < row_hi) p.ys[m * (p.N / 128) + gcol] = sc;
       }
-    // (ds ops of one wavefront complete in order: no barrier needed here)
-    constexpr int LANES_PER_ROW = TN * 2 / 16;
-    constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
-    static_assert(TM % ROWS_PER_PASS == 0, "whole passes");
-    const int c16 = lane % LANES_PER_ROW;
-    const bool epi_lane = lane < ROWS_PER_PASS * LANES_PER_ROW;
-#pragma unroll
-    for (int pass = 0; pass < TM / ROWS_PER_PASS; ++pass) {
-      const int mr = pass * ROWS_PER_PASS + (epi_lane ? lane / LANES_PER_ROW : 0);
-      const int64_t m = row_lo + wm * TM + mr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * EPI_PITCH + c16 * 16);
-      if (epi_lane && m < row_hi)
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + m * p.N + n0 + wn * TN + c16 * 8) = v;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < SM; ++j) {
-      const int64_t m = row_lo + wm * TM + j * 16 + (lane & 15);
-      if (m >= row_hi) continue;
-#pragma unroll
-      for (int i = 0; i < SN; ++i) {
-        const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
-        float* dst = static_cast<float*>(p.y) + m * p.N + n;
-        if (add_out) {
-          // K-split part: add into the zeroed output (hardware fp32 atomics)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[i][j][r]);
-        } else {
-          *reinterpret_cast<v4f*>(dst) = acc[i][j];
+      // (ds ops of one wavefront complete in order: no barrier needed here)
+  #pragma unroll
+      for (int pass = 0; pass < TMW / 8; ++pass) {
+        const int mr = pass * 8 + lane / 8;
+        const int64_t m = row_lo + roff + mr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * QP + (lane % 8) * 16);
+        if (m < row_hi)
+          *reinterpret_cast<u32x4*>(static_cast<uint8_t*>(p.y) + m * p.N + n0 + wn * TN + (lane % 8) * 16) = v;
+      }
+    } else if constexpr (BF16OUT) {
+      // Stage the wavefront's TM x TN block as bf16 rows in LDS (8 bytes per lane
+      // and sub-tile), then write whole row segments (TN*2 bytes = 16 lanes x 16 B).
+      uint8_t* epi = tiles + wave * TM * EPI_PITCH;
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j)
+  #pragma unroll
+        for (int i = 0; i < SN; ++i) {
+          const int mr = j * 16 + (lane & 15);
+          const int nc = i * 16 + 4 * (lane >> 4);
+          u32x2 o;
+          o[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
+          o[1] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<u32x2*>(epi + mr * EPI_PITCH + nc * 2) = o;
+        }
+      // (ds ops of one wavefront complete in order: no barrier needed here)
+      constexpr int LANES_PER_ROW = TN * 2 / 16;
+      constexpr int ROWS_PER_PASS = 64 / LANES_PER_ROW;
+      static_assert(TMW % ROWS_PER_PASS == 0, "whole passes");
+      const int c16 = lane % LANES_PER_ROW;
+      const bool epi_lane = lane < ROWS_PER_PASS * LANES_PER_ROW;
+  #pragma unroll
+      for (int pass = 0; pass < TMW / ROWS_PER_PASS; ++pass) {
+        const int mr = pass * ROWS_PER_PASS + (epi_lane ? lane / LANES_PER_ROW : 0);
+        const int64_t m = row_lo + roff + mr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(epi + mr * EPI_PITCH + c16 * 16);
+        if (epi_lane && m < row_hi)
+          *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + m * p.N + n0 + wn * TN + c16 * 8) = v;
+      }
+    } else {
+  #pragma unroll
+      for (int j = 0; j < SMW; ++j) {
+        const int64_t m = row_lo + roff + j * 16 + (lane & 15);
+        if (m >= row_hi) continue;
+  #pragma unroll
+        for (int i = 0; i < SN; ++i) {
+          const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
+          float* dst = static_cast<float*>(p.y) + m * p.N + n;
+          if (add_out) {
+            // K-split part: add into the zeroed output (hardware fp32 atomics)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[i][j][r]);
+          } else {
+            *reinterpret_cast<v4f*>(dst) = acc[i][j];
+          }
         }
       }
     }
+  };
+  if constexpr (GROUPED) {
+    // Only the row sub-tiles that hold rows of the segment are multiplied: the
+    // K loop is compiled for 1 .. SM sub-tiles and each wavefront runs the copy
+    // for its live rows (chosen once per tile; no branch inside the loop).  The
+    // last m-tile of every expert segment is partial, and multiplying its rows
+    // past the segment end cost 12% more FP8 work than the segments hold.
+    const int64_t live64 = row_hi - (row_lo + wm * TM);
+    const int live = __builtin_amdgcn_readfirstlane(static_cast<int>(live64 < 0 ? 0 : (live64 > TM ? TM : live64)));
+    const int smw = (live + 15) / 16;  // 0: no live row (the copy for one sub-tile, whose loop it skips)
+    auto pick = [&](auto self, auto kc) -> void {
+      constexpr int k = decltype(kc)::value;
+      if constexpr (k == 1) {
+        body(kc, wm * TM);
+      } else {
+        if (smw >= k)
+          body(kc, wm * TM);
+        else
+          self(self, std::integral_constant<int, k - 1>{});
+      }
+    };
+    pick(pick, std::integral_constant<int, SM>{});
+  } else {
+    body(std::integral_constant<int, SM>{}, wm * TM);
   }
 }
 
