@@ -58,6 +58,31 @@ def test_skewed_routing():
     check_bf16(_run(g, 3000, 128, torch.bfloat16, "fp8"), ref, "fp8 accum")
 
 
+def test_every_live_row_count_of_a_tile():
+    """Segments whose last 128-row tile holds 1 .. 128 rows in steps that hit
+    every count of live 16-row sub-tiles in both m-parts of the tile (sizes on
+    and beside the 16-row boundaries).  Each segment's rows equal, bit for bit,
+    the dense kernel on that segment alone (the same 128-K blocks and
+    promotion order), and the whole output is within the oracle's bound."""
+    sizes = [1, 15, 16, 17, 32, 33, 48, 49, 63, 64, 65, 80, 81, 96, 97, 112, 113, 127, 128, 129, 200, 255, 256, 0, 47]
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    N, K = 256, 384
+    g, r = _case(off, N, K, 41)
+    M = int(off[-1])
+    say(f"grouped live-row counts: {len(sizes)} segments, {M} rows, N={N}, K={K}")
+    y = _run(g, M, N, torch.float32, "fp8")
+    qa, sa, _, qb, sb = g
+    for e, (lo, hi) in enumerate(zip(off[:-1], off[1:])):
+        if hi == lo:
+            continue
+        yd = fp8.fp8_block_gemm(qa[lo:hi].contiguous(), sa[lo:hi].contiguous(), qb[e].contiguous(),
+                                sb[e].contiguous(), accum="fp8", out_dtype=torch.float32)
+        assert torch.equal(y[lo:hi], yd), f"segment {e} ({hi - lo} rows) differs from the dense kernel"
+    ref = gemm.grouped_gemm(*r)
+    check_bf16(_run(g, M, N, torch.bfloat16, "fp8"), ref, "fp8 accum, bf16")
+    check_f32(_run(g, M, N, torch.float32, "exact"), ref, "exact accum fp32")
+
+
 def test_single_group_matches_dense_kernel():
     off = np.array([0, 333])
     g, r = _case(off, 256, 384, 13)
