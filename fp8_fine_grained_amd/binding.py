@@ -36,6 +36,9 @@ _SIGS = {
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_quant_per_tensor": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p,
                              _c.c_void_p, _c.c_int, _c.c_void_p],
+    "fp8_quant_act_weight": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p,
+                             _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
+                             _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p],
     "fp8_quant_weight_128x128_dual": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
@@ -157,6 +160,29 @@ def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None, pow2=False):
                             _ptr(scales), _stream(stream))
     _check(fn, st)
     return q, scales
+
+
+def fp8_quant_act_weight(x, w, q_x=None, s_x=None, q_w=None, s_w=None, stream=None, pow2=False):
+    """1x128 quantisation of the row-contiguous ``x`` [M, K_x] and 128x128
+    quantisation of ``w`` [N, K_w] in one launch (fp8_quant_act_weight).
+    Returns ``(q_x, s_x, q_w, s_w)``, equal to fp8_quant_act_1x128(x) and
+    fp8_quant_weight_128x128(w)."""
+    _on_gpu(x, w)
+    M, Kx = x.shape
+    N, Kw = w.shape
+    if x.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("x and w must be row-contiguous")
+    dev = x.device
+    q_x = torch.empty((M, Kx), dtype=torch.uint8, device=dev) if q_x is None else q_x
+    s_x = torch.empty((M, Kx // 128), dtype=torch.float32, device=dev) if s_x is None else s_x
+    q_w = torch.empty((N, Kw), dtype=torch.uint8, device=dev) if q_w is None else q_w
+    s_w = torch.empty((N // 128, Kw // 128), dtype=torch.float32, device=dev) if s_w is None else s_w
+    _on_gpu(q_x, s_x, q_w, s_w)
+    st = lib().fp8_quant_act_weight(_ptr(x), _dtype_code(x.dtype), M, Kx, x.stride(0), _ptr(q_x), _ptr(s_x),
+                                    _ptr(w), _dtype_code(w.dtype), N, Kw, w.stride(0), _ptr(q_w), _ptr(s_w),
+                                    1 if pow2 else 0, _stream(stream))
+    _check("fp8_quant_act_weight", st)
+    return q_x, s_x, q_w, s_w
 
 
 def fp8_quant_per_tensor(x, layout="act", q=None, scales=None, stream=None):

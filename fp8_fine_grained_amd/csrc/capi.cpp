@@ -65,16 +65,41 @@ int quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t stride_m
   return FP8FG_ERR_UNSUPPORTED;
 }
 
-int quant_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w, uint8_t* q, float* scales,
-                 fp8fg_stream_t stream, bool pow2) {
+// Checks of a 128x128 weight quantisation: FP8FG_OK, an error status, or -1
+// when there is nothing to do (N == 0 or K == 0).
+int check_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w, const uint8_t* q,
+                 const float* scales) {
   if (!valid_dtype(w_dtype) || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
-  if (N == 0 || K == 0) return FP8FG_OK;
+  if (N == 0 || K == 0) return -1;
   if (N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
   if (!w || !q || !scales) return FP8FG_ERR_INVALID_ARG;
   if (ld_w < K) return FP8FG_ERR_INVALID_ARG;
   if ((N / 128) * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scales, 4) || (ld_w * elem_size(w_dtype)) % 16 != 0)
     return FP8FG_ERR_MISALIGNED;
+  return FP8FG_OK;
+}
+
+// Checks of a 1x128 quantisation of a row-contiguous activation (ld_x >= K):
+// FP8FG_OK, an error status, or -1 when there is nothing to do.
+int check_act_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ld_x, const uint8_t* q,
+                   const float* scales) {
+  if (!valid_dtype(x_dtype) || M < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
+  if (M == 0 || K == 0) return -1;
+  if (K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
+  if (!x || !q || !scales) return FP8FG_ERR_INVALID_ARG;
+  if (ld_x < K) return FP8FG_ERR_INVALID_ARG;
+  if (M > kInt32Max || K > kInt32Max || M * (K / 128) > kInt32Max) return FP8FG_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(scales, 4) || !aligned(x, 16) || (ld_x * elem_size(x_dtype)) % 16 != 0)
+    return FP8FG_ERR_MISALIGNED;
+  return FP8FG_OK;
+}
+
+int quant_weight(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w, uint8_t* q, float* scales,
+                 fp8fg_stream_t stream, bool pow2) {
+  const int c = check_weight(w, w_dtype, N, K, ld_w, q, scales);
+  if (c < 0) return FP8FG_OK;
+  if (c != FP8FG_OK) return c;
   return hip_status(fp8fg::launch_quant_weight(w, w_dtype == FP8FG_BF16, pow2, N, K, ld_w, q, scales,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -101,6 +126,23 @@ int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, i
 int fp8_quant_weight_128x128_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                                   uint8_t* q, float* scales, fp8fg_stream_t stream) {
   return quant_weight(w, w_dtype, N, K, ld_w, q, scales, stream, true);
+}
+
+int fp8_quant_act_weight(const void* x, int x_dtype, int64_t M, int64_t K_x, int64_t ld_x, uint8_t* q_x,
+                         float* s_x, const void* w, int w_dtype, int64_t N, int64_t K_w, int64_t ld_w,
+                         uint8_t* q_w, float* s_w, int pow2, fp8fg_stream_t stream) {
+  if (pow2 != 0 && pow2 != 1) return FP8FG_ERR_INVALID_ARG;
+  const int cx = check_act_rows(x, x_dtype, M, K_x, ld_x, q_x, s_x);
+  const int cw = check_weight(w, w_dtype, N, K_w, ld_w, q_w, s_w);
+  if (cx > 0) return cx;
+  if (cw > 0) return cw;
+  if (cx < 0 && cw < 0) return FP8FG_OK;
+  // an empty part launches no workgroups
+  if (cx < 0) M = 0;
+  if (cw < 0) N = 0;
+  return hip_status(fp8fg::launch_quant_act_weight(x, x_dtype == FP8FG_BF16, M, K_x, ld_x, q_x, s_x, w,
+                                                   w_dtype == FP8FG_BF16, N, K_w, ld_w, q_w, s_w, pow2 == 1,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 int fp8_quant_per_tensor(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ld, uint8_t* q,

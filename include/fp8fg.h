@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 7
+#define FP8FG_ABI_VERSION 8
 
 /* Status codes returned by every entry point. */
 enum {
@@ -176,6 +176,30 @@ int fp8_quant_weight_128x128(const void* w, int w_dtype, int64_t N, int64_t K, i
 /* The same with power-of-two block scales (rule as fp8_quant_act_1x128_pow2). */
 int fp8_quant_weight_128x128_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                                   uint8_t* q, float* scales, fp8fg_stream_t stream);
+
+/*
+ * A layer step's two quantisations in one launch: the 1x128 quantisation of a
+ * row-contiguous activation and the 128x128 quantisation of a weight (the
+ * passages of fp8_quant_act_1x128 and fp8_quant_weight_128x128).  Every code
+ * and scale equals what those two calls write; one launch instead of two saves
+ * a kernel ramp and tail (X [4096,7168] + W [7168,7168] bf16: 38 us against
+ * 43 us).
+ *
+ * x, x_dtype, M, K_x   activation [M, K_x], row pitch ld_x >= K_x elements
+ *                      (the row-contiguous layout of fp8_quant_act_1x128).
+ * q_x, s_x             out, codes [M, K_x] and scales [M, K_x/128].
+ * w, w_dtype, N, K_w   weight [N, K_w], row pitch ld_w >= K_w elements.
+ * q_w, s_w             out, codes [N, K_w] and scales [N/128, K_w/128].
+ * pow2                 0: scales amax/448; 1: power-of-two scales (the rule of
+ *                      the *_pow2 quantisers), for both tensors.
+ * Requirements of each part as in the separate calls; an empty part (M == 0,
+ * N == 0 or a zero K) is skipped and its pointers are not read.  The two parts
+ * must not overlap.  If either part is invalid nothing is launched and its
+ * status is returned (the activation's first).
+ */
+int fp8_quant_act_weight(const void* x, int x_dtype, int64_t M, int64_t K_x, int64_t ld_x, uint8_t* q_x,
+                         float* s_x, const void* w, int w_dtype, int64_t N, int64_t K_w, int64_t ld_w,
+                         uint8_t* q_w, float* s_w, int pow2, fp8fg_stream_t stream);
 
 /*
  * 128x128 weight quantisation that also writes the transposed operand, for the

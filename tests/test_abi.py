@@ -22,6 +22,7 @@ def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
                           "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual", "fp8_quant_per_tensor",
+                          "fp8_quant_act_weight",
                           "fp8_block_gemm", "fp8_block_gemm_accum", "fp8_block_gemm_quant", "fp8_block_grouped_gemm",
                           "fp8_block_grouped_gemm_accum", "fp8_block_grouped_gemm_gather",
                           "fp8fg_status_string", "fp8fg_abi_version"}
@@ -30,7 +31,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 7
+    assert L.fp8fg_abi_version() == 8
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -78,6 +79,32 @@ def test_quant_per_tensor_validation(L):
     assert f(*args(x=BAD)) == fp8.ERR_MISALIGNED
     assert f(*args(s=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
     assert f(*args(ld=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
+
+
+def test_quant_act_weight_validation(L):
+    """Each part is checked as in its separate call; an invalid part launches
+    nothing (every call here either fails validation or has two empty parts)."""
+    f = L.fp8_quant_act_weight
+    ok = dict(x=GOOD, xdt=fp8.BF16, M=4, Kx=256, ldx=256, qx=GOOD, sx=GOOD,
+              w=GOOD, wdt=fp8.BF16, N=128, Kw=256, ldw=256, qw=GOOD, sw=GOOD, pow2=0, stream=NULL)
+    args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
+    assert f(*args(x=NULL, M=0, qx=NULL, sx=NULL, w=NULL, N=0, qw=NULL, sw=NULL)) == fp8.OK  # both empty
+    assert f(*args(pow2=2)) == fp8.ERR_INVALID_ARG
+    assert f(*args(xdt=7)) == fp8.ERR_INVALID_ARG
+    assert f(*args(wdt=7)) == fp8.ERR_INVALID_ARG
+    assert f(*args(M=-1)) == fp8.ERR_INVALID_ARG
+    assert f(*args(Kx=200, ldx=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(N=100)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(x=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(sw=NULL)) == fp8.ERR_INVALID_ARG
+    assert f(*args(ldx=128)) == fp8.ERR_INVALID_ARG  # ld_x < K_x
+    assert f(*args(ldw=128)) == fp8.ERR_INVALID_ARG  # ld_w < K_w
+    assert f(*args(qx=BAD)) == fp8.ERR_MISALIGNED
+    assert f(*args(sw=ctypes.c_void_p(0x10002))) == fp8.ERR_MISALIGNED
+    assert f(*args(ldw=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
+    # an invalid part is reported even when the other part is empty
+    assert f(*args(w=NULL, N=0, qw=NULL, sw=NULL, Kx=200, ldx=200)) == fp8.ERR_UNSUPPORTED
+    assert f(*args(x=NULL, M=0, qx=NULL, sx=NULL, N=100)) == fp8.ERR_UNSUPPORTED
 
 
 def test_quant_weight_dual_validation(L):

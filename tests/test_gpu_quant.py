@@ -176,6 +176,55 @@ def test_weight_dual_small():
     _weight_dual(torch.from_numpy(_special_tiles()[:8].reshape(8, 1024).repeat(16, axis=0)[:128]), "special")
 
 
+def _act_weight(x, w, pow2, what, oracle=False):
+    """The one-launch pair against the two separate calls, bit for bit, with
+    guard bands around all four outputs; optionally against the oracle too."""
+    say(f"quant_act_weight {what}: x {tuple(x.shape)} {x.dtype}, w {tuple(w.shape)} {w.dtype}, pow2={pow2}")
+    M, Kx = x.shape
+    N, Kw = w.shape
+    bufs = [guarded((M, Kx), torch.uint8), guarded((M, Kx // 128), torch.float32),
+            guarded((N, Kw), torch.uint8), guarded((N // 128, Kw // 128), torch.float32)]
+    xd, wd = x.cuda(), w.cuda()
+    fp8.fp8_quant_act_weight(xd, wd, *[v for _, v in bufs], pow2=pow2)
+    torch.cuda.synchronize()
+    for b, _ in bufs:
+        check_guard(b)
+    qx, sx, qw, sw = (v for _, v in bufs)
+    if M:
+        rx, rsx = fp8.fp8_quant_act_1x128(xd, pow2=pow2)
+        assert torch.equal(qx, rx) and torch.equal(sx.view(torch.int32), rsx.view(torch.int32)), what + " act"
+    if N:
+        rw, rsw = fp8.fp8_quant_weight_128x128(wd, pow2=pow2)
+        assert torch.equal(qw, rw) and torch.equal(sw.view(torch.int32), rsw.view(torch.int32)), what + " weight"
+    if oracle:
+        q_ref, s_ref = quant.quant_1x128(f32(x))
+        assert_codes_equal(qx, q_ref, what + " act")
+        assert_scales_equal(sx, s_ref, what + " act")
+        q_ref, s_ref = quant.quant_128x128(f32(w))
+        assert_codes_equal(qw, q_ref, what + " weight")
+        assert_scales_equal(sw, s_ref, what + " weight")
+
+
+def test_act_weight_one_launch():
+    d = workloads.dense(seed=21, M=300, N=256, K=512)  # 1200 activation tiles: a partial last workgroup
+    x, w = d["x"], d["w"]
+    _act_weight(x, w, False, "bf16 / bf16", oracle=True)
+    _act_weight(x, w, True, "bf16 / bf16, power-of-two scales")
+    _act_weight(x.float(), w, False, "fp32 / bf16")
+    _act_weight(x, w.float(), False, "bf16 / fp32")
+    t = workloads.tiny()
+    _act_weight(t["x"], t["w"], False, "tiny fp32 / fp32", oracle=True)
+    _act_weight(torch.from_numpy(_special_tiles()), w[:, :384].contiguous(), False, "special tiles, K 1024 / 384",
+                oracle=True)
+    _act_weight(x[:0], w, False, "no activation rows")
+    _act_weight(x, w[:0], False, "no weight rows")
+
+
+def test_act_weight_one_launch_dense_shape():
+    d = workloads.dense()
+    _act_weight(d["x"], d["w"], False, "X [4096,7168] + W [7168,7168] bf16")
+
+
 def test_cast_exhaustive_through_the_act_quantiser():
     """Every fp32 in [0, 448] and its negation through the 1x128 kernel's cast.
 
