@@ -316,19 +316,19 @@ def bench_pow2(args, torch, fp8, workloads):
     promotion step)."""
     M, N, K = 4096, 7168, 7168
     d = workloads.dense()
-    xs = [d["x"].cuda() for _ in range(3)]
-    ws = [d["w"].cuda() for _ in range(3)]
+    nx, nw = _copies(M * K * 2), _copies(N * K * 2)
+    xs = [d["x"].cuda() for _ in range(nx)]
+    ws = [d["w"].cuda() for _ in range(nw)]
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
     sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     t_gemm = Timer(torch, args.steps)
-    t_act, t_w = Timer(torch, 1), Timer(torch, 1)
+    t_aw, t_act, t_w = Timer(torch, 1), Timer(torch, 1), Timer(torch, 1)
 
     def step(i, timed):
-        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa, pow2=True)
-        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb, pow2=True)
+        fp8.fp8_quant_act_weight(xs[i % nx], ws[i % nw], qa, sa, qb, sb, pow2=True)
         if timed:
             with t_gemm:
                 fp8.fp8_block_gemm(qa, sa, qb, sb, accum="scaled", y=y)
@@ -344,12 +344,15 @@ def bench_pow2(args, torch, fp8, workloads):
         step(i, True)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    with t_aw:
+        for i in range(args.steps):
+            fp8.fp8_quant_act_weight(xs[i % nx], ws[i % nw], qa, sa, qb, sb, pow2=True)
     with t_act:
         for i in range(args.steps):
-            fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa, pow2=True)
+            fp8.fp8_quant_act_1x128(xs[i % nx], qa, sa, pow2=True)
     with t_w:
         for i in range(args.steps):
-            fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb, pow2=True)
+            fp8.fp8_quant_weight_128x128(ws[i % nw], qb, sb, pow2=True)
     torch.cuda.synchronize()
     flop = 2.0 * M * N * K
     gemm_ms = t_gemm.mean_ms()
@@ -361,11 +364,14 @@ def bench_pow2(args, torch, fp8, workloads):
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
         "config": {"workload": "dense projection with power-of-two (E8M0) group scales: quantise X bf16 [4096,7168] "
-                               "per 1x128 and W bf16 [7168,7168] per 128x128, scaled-MFMA GEMM Y = X W^T, bf16 out",
-                   "M": M, "N": N, "K": K, "accum": "scaled_mfma", "input_copies_rotated": 3},
+                               "per 1x128 and W bf16 [7168,7168] per 128x128 (one launch), scaled-MFMA GEMM "
+                               "Y = X W^T, bf16 out",
+                   "M": M, "N": N, "K": K, "accum": "scaled_mfma", "input_copies_rotated": {"X": nx, "W": nw}},
         "kernels": {
-            "fp8_quant_act_1x128_pow2": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
-            "fp8_quant_weight_128x128_pow2": _hbm_line("w", t_w.mean_ms() / args.steps, w_bytes, {}),
+            "fp8_quant_act_weight, pow2 (X + W, the step's launch)": _hbm_line(
+                "aw", t_aw.mean_ms() / args.steps, act_bytes + w_bytes, {}),
+            "fp8_quant_act_1x128_pow2 (separate launch)": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
+            "fp8_quant_weight_128x128_pow2 (separate launch)": _hbm_line("w", t_w.mean_ms() / args.steps, w_bytes, {}),
             "fp8_block_gemm (scaled)": {"ms": gemm_ms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS,
                                         "ms_percentiles": t_gemm.percentiles_ms()},
         },
@@ -384,8 +390,9 @@ def bench_fused(args, torch, fp8, workloads):
     is timed afterwards; both give the same bytes."""
     M, N, K = 4096, 7168, 7168
     d = workloads.dense()
-    xs = [d["x"].cuda() for _ in range(3)]
-    ws = [d["w"].cuda() for _ in range(3)]
+    nx, nw = _copies(M * K * 2), _copies(N * K * 2)
+    xs = [d["x"].cuda() for _ in range(nx)]
+    ws = [d["w"].cuda() for _ in range(nw)]
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
@@ -396,8 +403,7 @@ def bench_fused(args, torch, fp8, workloads):
     t_f, t_g, t_q = Timer(torch, args.steps), Timer(torch, args.steps), Timer(torch, args.steps)
 
     def step(i, timed):
-        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
-        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+        fp8.fp8_quant_act_weight(xs[i % nx], ws[i % nw], qa, sa, qb, sb)
         if timed:
             with t_f:
                 fp8.fp8_block_gemm_quant(qa, sa, qb, sb, q=qy, scales=sy)
@@ -416,8 +422,7 @@ def bench_fused(args, torch, fp8, workloads):
     # unfused: the same step with fp32 Y written, then quantised by the 1x128 quantiser
     t1 = time.perf_counter()
     for i in range(args.steps):
-        fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
-        fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+        fp8.fp8_quant_act_weight(xs[i % nx], ws[i % nw], qa, sa, qb, sb)
         with t_g:
             fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y32)
         with t_q:
@@ -434,7 +439,7 @@ def bench_fused(args, torch, fp8, workloads):
         "config": {"workload": "dense projection with the output quantised for the next layer: quantise X bf16 "
                                "[4096,7168] 1x128 and W bf16 [7168,7168] 128x128, GEMM Y = X W^T whose epilogue "
                                "writes Y as E4M3 codes [4096,7168] + fp32 scales [4096,56]",
-                   "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": 3},
+                   "M": M, "N": N, "K": K, "accum": "fp8_mfma", "input_copies_rotated": {"X": nx, "W": nw}},
         "kernels": {
             "fp8_block_gemm_quant": {"ms": fms, "TFLOP/s": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS},
             "unfused: fp8_block_gemm (fp32 out)": {"ms": t_g.mean_ms()},
@@ -586,8 +591,9 @@ def bench_pertensor(args, torch, fp8, workloads):
     d = workloads.dense()
     M, K = d["x"].shape
     N = d["w"].shape[0]
-    xs = [d["x"].cuda() for _ in range(3)]
-    ws = [d["w"].cuda() for _ in range(3)]
+    nx, nw = _copies(M * K * 2), _copies(N * K * 2)
+    xs = [d["x"].cuda() for _ in range(nx)]
+    ws = [d["w"].cuda() for _ in range(nw)]
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
@@ -598,14 +604,14 @@ def bench_pertensor(args, torch, fp8, workloads):
     def step(i, timed):
         if timed:
             with tx:
-                fp8.fp8_quant_per_tensor(xs[i % 3], "act", qa, sa)
+                fp8.fp8_quant_per_tensor(xs[i % nx], "act", qa, sa)
             with tw:
-                fp8.fp8_quant_per_tensor(ws[i % 3], "weight", qb, sb)
+                fp8.fp8_quant_per_tensor(ws[i % nw], "weight", qb, sb)
             with tg:
                 fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
         else:
-            fp8.fp8_quant_per_tensor(xs[i % 3], "act", qa, sa)
-            fp8.fp8_quant_per_tensor(ws[i % 3], "weight", qb, sb)
+            fp8.fp8_quant_per_tensor(xs[i % nx], "act", qa, sa)
+            fp8.fp8_quant_per_tensor(ws[i % nw], "weight", qb, sb)
             fp8.fp8_block_gemm(qa, sa, qb, sb, accum="fp8", y=y)
 
     for i in range(args.warmup):
@@ -619,10 +625,10 @@ def bench_pertensor(args, torch, fp8, workloads):
     fa, fw = Timer(torch, 1), Timer(torch, 1)
     with fa:
         for i in range(args.steps):
-            fp8.fp8_quant_act_1x128(xs[i % 3], qa, sa)
+            fp8.fp8_quant_act_1x128(xs[i % nx], qa, sa)
     with fw:
         for i in range(args.steps):
-            fp8.fp8_quant_weight_128x128(ws[i % 3], qb, sb)
+            fp8.fp8_quant_weight_128x128(ws[i % nw], qb, sb)
     flop = 2.0 * M * N * K
     gms = tg.mean_ms()
     tf = flop / (gms * 1e-3) / 1e12
@@ -633,7 +639,7 @@ def bench_pertensor(args, torch, fp8, workloads):
         "data": "synthetic",
         "config": {"workload": "dense projection X bf16 [4096,7168] (0.1% x100), W bf16 [7168,7168], one scale per "
                                "tensor (amax pass + cast), block-scaled FP8 GEMM with uniform scales, bf16 out",
-                   "M": M, "N": N, "K": K, "input_copies_rotated": 3},
+                   "M": M, "N": N, "K": K, "input_copies_rotated": {"X": nx, "W": nw}},
         "kernels": {
             "fp8_quant_per_tensor (X, 3 launches)": {"ms": tx.mean_ms()},
             "fp8_quant_per_tensor (W, 3 launches)": {"ms": tw.mean_ms()},
@@ -842,8 +848,9 @@ def bench_dgrad(args, torch, fp8, workloads):
     # once for both orientations, the GEMM reads the transposed codes.
     M, N, K = 4096, 7168, 7168
     d = workloads.dgrad()
-    dys = [d["dy"].cuda() for _ in range(3)]
-    ws = [d["w"].cuda() for _ in range(3)]
+    ndy, nw = _copies(M * N * 2), _copies(N * K * 2)
+    dys = [d["dy"].cuda() for _ in range(ndy)]
+    ws = [d["w"].cuda() for _ in range(nw)]
     qa = torch.empty((M, N), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, N // 128), dtype=torch.float32, device="cuda")
     q = torch.empty((N, K), dtype=torch.uint8, device="cuda")
@@ -855,8 +862,8 @@ def bench_dgrad(args, torch, fp8, workloads):
     t_act, t_w = Timer(torch, 1), Timer(torch, 1)
 
     def step(i, timed):
-        fp8.fp8_quant_act_1x128(dys[i % 3], qa, sa)
-        fp8.fp8_quant_weight_128x128_dual(ws[i % 3], q, s, qt, st)
+        fp8.fp8_quant_act_1x128(dys[i % ndy], qa, sa)
+        fp8.fp8_quant_weight_128x128_dual(ws[i % nw], q, s, qt, st)
         if timed:
             with t_gemm:
                 fp8.fp8_block_gemm(qa, sa, qt, st, accum="fp8", y=y)
@@ -874,10 +881,10 @@ def bench_dgrad(args, torch, fp8, workloads):
     dt = (time.perf_counter() - t0) / args.steps
     with t_act:
         for i in range(args.steps):
-            fp8.fp8_quant_act_1x128(dys[i % 3], qa, sa)
+            fp8.fp8_quant_act_1x128(dys[i % ndy], qa, sa)
     with t_w:
         for i in range(args.steps):
-            fp8.fp8_quant_weight_128x128_dual(ws[i % 3], q, s, qt, st)
+            fp8.fp8_quant_weight_128x128_dual(ws[i % nw], q, s, qt, st)
     torch.cuda.synchronize()
     flop = 2.0 * M * N * K
     gms = t_gemm.mean_ms()
@@ -890,7 +897,7 @@ def bench_dgrad(args, torch, fp8, workloads):
         "config": {"workload": "data gradient dX = dY W of the dense projection: dY bf16 [4096,7168] ~ N(0,1e-3) "
                                "quantised 1x128, W bf16 [7168,7168] quantised 128x128 with the transposed codes "
                                "written in the same pass, block-scaled GEMM on W^T, bf16 out",
-                   "M": M, "N": K, "K": N, "input_copies_rotated": 3},
+                   "M": M, "N": K, "K": N, "input_copies_rotated": {"dY": ndy, "W": nw}},
         "kernels": {
             "fp8_quant_act_1x128": _hbm_line("act", t_act.mean_ms() / args.steps, act_bytes, {}),
             "fp8_quant_weight_128x128_dual": _hbm_line("dual", t_w.mean_ms() / args.steps, dual_bytes, {}),
