@@ -737,6 +737,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
           if constexpr (EXACT) wn_frag = widen(fn);
   #pragma unroll
           for (int j = 0; j < SMW; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
+          if constexpr (!GROUPED && (EXACT || !ROWS)) {
+            // Tie the previous step's partials to this point: without it the
+            // compiler promotes each partial right after its own MFMA (fewer
+            // live registers) and the FMAs wait on the matrix core (s_nop);
+            // here they read results four MFMAs old.  Dense 4096 x 7168 x 7168
+            // 193.4 -> 190.6 us, exact weight gradient 1630 -> 1586 us; no gain
+            // on the grouped or the row-scaled FP8 tiles, which keep the
+            // compiler's order.
+            if (i > 0) {
+#pragma unroll
+              for (int j = 0; j < SMW; ++j) asm volatile("" : "+v"(P[(i - 1) & 1][j]));
+            }
+          }
           if (i > 0)
             promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
           else if (DEFER && kb > 0)
