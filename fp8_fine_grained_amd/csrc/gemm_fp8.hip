@@ -584,7 +584,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       for (int kb = 0; kb < KB; ++kb) {
         const int st_fill = st == 0 ? STAGES - 1 : st - 1;
         const int kb_fill = clampkb(kb + STAGES - 1);
-  #pragma unroll
+#pragma unroll
         for (int d = 0; d < ND; ++d) dma_tile(d, kb_fill, st_fill);
         if (STAGES > 2 || uwave < SA_WAVES + SB_WAVES) dma_scale(kb_fill, st_fill);
         prefetch(clampkb(kb + PF));
@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     };
     {
       const uint8_t* tA = tiles;
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j) {
         fm[j] = frag(tA, roff + j * 16, lane);
         if constexpr (SCALED)
@@ -653,7 +653,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       } else {
         (void)b;
         v4f r = z;
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < 4; ++q) r = __builtin_amdgcn_mfma_f32_16x16x32_f16(wb.q[q], wm_frag[j].q[q], r, 0, 0, 0);
         return r;
       }
@@ -661,10 +661,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     // acc[i] += P * factor, with the row scales of sub-tile i in row mode, or the
     // block scale bs of sub-tile i for unaligned weight tiles.
     auto promote = [&](v4f* a, const v4f (&P)[SMW], const float (&fv)[SMW], const v4f& sbr, float bs) {
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j) {
         const float fj = BALIGN ? fv[j] : fv[j] * bs;
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (ROWS)
             a[j][r] = fmaf(P[j][r] * sbr[r], fv[j], a[j][r]);
@@ -696,23 +696,23 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       const int kb_fill = clampkb(kb + STAGES - 1);
       const uint8_t* tB = tiles + st * STAGE + TILE_A;
       if constexpr (!BALIGN) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < SN; ++i) sbv[i] = sub_scale(st, i);
       }
       if constexpr (EXACT) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < SMW; ++j) wm_frag[j] = widen(fm[j]);
       }
       __builtin_amdgcn_s_setprio(1);  // the issuing phase of the matrix cores goes first
       // Sub-tile steps 0 .. SN-2: the fragment of step i+1 is read from LDS while
       // the MFMAs of step i run, and the promotion FMAs of step i-1 (double-
       // buffered partials) fill the VALU under them.
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < SN - 1; ++i) {
         // The loads of the block being prefetched go out over the first SPREAD
         // sub-tile steps, between MFMAs.
         if (i < SPREAD) {
-  #pragma unroll
+#pragma unroll
           for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
         }
         if (i == 0) {
@@ -730,12 +730,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
         if constexpr (ROWS) sbr[i & 1] = row_scales(st, i);
         if constexpr (SCALED) {
           const int ewi = BALIGN ? ew : e8m0(bsv(i));
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < SMW; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
         } else {
           WideFrag wn_frag;
           if constexpr (EXACT) wn_frag = widen(fn);
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < SMW; ++j) P[i & 1][j] = partial(fn, wn_frag, j);
           if constexpr (!GROUPED && (EXACT || !ROWS)) {
             // Tie the previous step's partials to this point: without it the
@@ -775,7 +775,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       if constexpr (SCALED) {
         const uint8_t* tA = tiles + st * STAGE;
         const int ew_old = BALIGN ? ew : e8m0(bsv(SN - 1));
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < SMW; ++j) {
           acc[SN - 1][j] = mma_scaled(fn, fm[j], acc[SN - 1][j], ew_old, ex[j]);
           // (After the final block this reads a stage nobody uses; the values are dropped.)
@@ -788,13 +788,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
         continue;
       }
       float f_old[SMW];
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j) f_old[j] = f[j];
       {
         const uint8_t* tA = tiles + st * STAGE;
         WideFrag wn_frag;
         if constexpr (EXACT) wn_frag = widen(fn);
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < SMW; ++j) {
           P[(SN - 1) & 1][j] = partial(fn, wn_frag, j);
           // (After the final block this reads a stage nobody uses; the values are dropped.)
@@ -806,7 +806,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       }
       promote(acc[SN - 2], P[(SN - 2) & 1], f_old, sbr[(SN - 2) & 1], bsv(SN - 2));
       if constexpr (DEFER) {
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < SMW; ++j) f_prev[j] = f_old[j];
       } else {
         promote(acc[SN - 1], P[(SN - 1) & 1], f_old, sbr[(SN - 1) & 1], bsv(SN - 1));
@@ -829,19 +829,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       static_assert(NW * TM * QP <= TILES_BYTES, "staging fits the tile buffers");
       uint8_t* epi = tiles + wave * TM * QP;
       const int64_t gcol = (n0 + wn * TN) / 128;  // group index along N
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j) {
         float am = 0.0f;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < SN; ++i)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) am = fmaxf(am, fabsf(acc[i][j][r]));
         am = fmaxf(am, __shfl_xor(am, 16));
         am = fmaxf(am, __shfl_xor(am, 32));
         float sc, inv;
         group_scale<QOUT == 2>(am, sc, inv);
         const int mr = j * 16 + (lane & 15);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < SN; ++i)
           *reinterpret_cast<uint32_t*>(epi + mr * QP + i * 16 + 4 * (lane >> 4)) =
               cvt4(acc[i][j][0] * inv, acc[i][j][1] * inv, acc[i][j][2] * inv, acc[i][j][3] * inv);
@@ -849,7 +849,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
         if (lane < 16 && m < row_hi) p.ys[m * (p.N / 128) + gcol] = sc;
       }
       // (ds ops of one wavefront complete in order: no barrier needed here)
-  #pragma unroll
+#pragma unroll
       for (int pass = 0; pass < TMW / 8; ++pass) {
         const int mr = pass * 8 + lane / 8;
         const int64_t m = row_lo + roff + mr;
@@ -861,9 +861,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       // Stage the wavefront's TM x TN block as bf16 rows in LDS (8 bytes per lane
       // and sub-tile), then write whole row segments (TN*2 bytes = 16 lanes x 16 B).
       uint8_t* epi = tiles + wave * TM * EPI_PITCH;
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < SN; ++i) {
           const int mr = j * 16 + (lane & 15);
           const int nc = i * 16 + 4 * (lane >> 4);
@@ -878,7 +878,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       static_assert(TMW % ROWS_PER_PASS == 0, "whole passes");
       const int c16 = lane % LANES_PER_ROW;
       const bool epi_lane = lane < ROWS_PER_PASS * LANES_PER_ROW;
-  #pragma unroll
+#pragma unroll
       for (int pass = 0; pass < TMW / ROWS_PER_PASS; ++pass) {
         const int mr = pass * ROWS_PER_PASS + (epi_lane ? lane / LANES_PER_ROW : 0);
         const int64_t m = row_lo + roff + mr;
@@ -887,17 +887,17 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
           *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + m * p.N + n0 + wn * TN + c16 * 8) = v;
       }
     } else {
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < SMW; ++j) {
         const int64_t m = row_lo + roff + j * 16 + (lane & 15);
         if (m >= row_hi) continue;
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < SN; ++i) {
           const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
           float* dst = static_cast<float*>(p.y) + m * p.N + n;
           if (add_out) {
             // K-split part: add into the zeroed output (hardware fp32 atomics)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 4; ++r) unsafeAtomicAdd(dst + r, acc[i][j][r]);
           } else {
             *reinterpret_cast<v4f*>(dst) = acc[i][j];
