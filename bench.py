@@ -17,11 +17,11 @@ dual weight quantiser, each rotated the same way.  Before the W warm-up steps
 the step runs back to back for --settle seconds (default 1): a cold GPU's
 clocks take ~100 GEMMs to come up, which a long training run never sees.
 
-Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused``) measure the remaining rows of
-the path and print their own JSON line; the default run prints exactly one line.
+Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor``) measure the
+remaining rows of the path and print their own JSON line; the default run prints exactly one line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense|quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor]
-                    [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
+                    [--workload dense|quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor] [--no-cpu-baseline]
 """
 
 import argparse
