@@ -56,3 +56,56 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for got, want in zip((qa, sa, qb, sb, y), eager):
             assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep} differs"
+
+
+def test_graph_dense_step_and_k_split_replays():
+    """The dense projection step at its full size (one-launch X + W quantiser,
+    FP8 GEMM with bf16 output) and an fp32 GEMM whose partial last round runs as
+    K-split parts (zero-fill kernel plus fp32 atomic adds), captured in one graph.
+    The bf16 step replays bit for bit; the K-split output's split tiles add their
+    parts in completion order, so each replay matches the eager result to the
+    last bits of those sums (and exactly everywhere else)."""
+    d = workloads.dense()
+    x, w = d["x"].cuda(), d["w"].cuda()
+    M, K = x.shape
+    N = w.shape[0]
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    qb = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    # 4352 x 4096 x 1024 in exact mode: 544 tiles of 128 x 256, the last 32 in 8 K parts each
+    s = workloads.dense(M=4352, N=4096, K=1024)
+    qs, ss = fp8.fp8_quant_act_1x128(s["x"].cuda())
+    qv, sv = fp8.fp8_quant_weight_128x128(s["w"].cuda())
+    ys = torch.empty((4352, 4096), dtype=torch.float32, device="cuda")
+
+    def step():
+        fp8.fp8_quant_act_weight(x, w, qa, sa, qb, sb)
+        fp8.fp8_block_gemm(qa, sa, qb, sb, y=y)
+        fp8.fp8_block_gemm(qs, ss, qv, sv, accum="exact", y=ys)
+
+    say("dense step + K-split fp32 GEMM, eager")
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (qa, sa, qb, sb, y, ys)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    outs = (qa, sa, qb, sb, y, ys)
+    for rep in range(4):
+        say(f"replay {rep}")
+        for t_ in outs:
+            t_.fill_(7)  # eager work between replays: the replay must rewrite every output
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs[:5], eager[:5]):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep} differs"
+        diff = (ys - eager[5]).abs()
+        assert torch.all(diff <= 1e-6 * eager[5].abs() + 1e-7 * float(eager[5].abs().max())), \
+            f"replay {rep}: K-split output differs beyond the addition order"
+        same = float((diff == 0).float().mean())
+        say(f"  K-split output: {100 * same:.1f}% of elements bit-identical")
+        assert same >= 0.9  # only the 32 split tiles (32 of 544) may differ
