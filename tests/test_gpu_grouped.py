@@ -7,7 +7,7 @@ import torch
 import workloads
 from fp8_fine_grained_amd import binding as fp8
 from oracle import gemm, quant
-from tests.gpu_util import check_bf16, check_f32, check_guard, f32, guarded, say
+from tests.gpu_util import assert_codes_equal, assert_scales_equal, check_bf16, check_f32, check_guard, f32, guarded, say
 
 pytestmark = pytest.mark.gpu
 
@@ -166,9 +166,12 @@ def test_empty_inputs_are_noops():
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_full_moe_up_projection():
-    """Full MoE size; the first and the last row of every expert's segment (and
-    one row inside it) against the oracle, which quantises all 256 expert
-    weights itself (in spawned worker processes, one expert each)."""
+    """Full MoE size, every output: the routed rows' codes and scales bit-exact
+    (the oracle quantises the 8192 tokens; a routed row is its token's row), each
+    expert's weight codes and scales bit-exact, and all 65536 x 2048 outputs
+    within the bf16 tolerance of the oracle's fp64 grouped GEMM (each expert's
+    segment in a spawned worker process, which quantises that expert's weight
+    itself)."""
     import hashlib
     import multiprocessing
     import os
@@ -192,31 +195,29 @@ def test_full_moe_up_projection():
     qb, sb = qb.view(256, 2048, 7168), sb.view(256, 16, 56)
     y = fp8.fp8_block_grouped_gemm(qa, sa, torch.from_numpy(offsets).cuda(), qb, sb)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    seg_rows = {}
+    say("  oracle: quantise the tokens")
+    rt, rst = quant.quant_1x128(f32(tokens))
+    permn = np.asarray(route["perm"])
+    assert_codes_equal(qa, rt[permn], "routed row codes")
+    assert_scales_equal(sa, rst[permn], "routed row scales")
+    jobs = []
     for e in range(256):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
-            seg_rows[e] = sorted({lo, hi - 1, int(rng.integers(lo, hi))})
-    rows = np.array(sorted(r for rs in seg_rows.values() for r in rs))
-    ra, rsa = quant.quant_1x128(f32(tokens[perm[rows]]))
-    assert np.array_equal(qa[torch.from_numpy(rows).cuda()].cpu().numpy(), ra)
-    pos = {int(r): i for i, r in enumerate(rows)}
-    jobs = [(e, ra[[pos[r] for r in rs]], rsa[[pos[r] for r in rs]]) for e, rs in seg_rows.items()]
+            jobs.append((e, rt[permn[lo:hi]], rst[permn[lo:hi]]))
     nproc = max(1, min(16, len(os.sched_getaffinity(0))))
-    say(f"  oracle: {len(jobs)} experts in {nproc} worker processes, {rows.size} rows")
-    results = []
+    say(f"  oracle: {len(jobs)} experts in {nproc} worker processes, all {int(offsets[-1])} rows")
+    ref = np.zeros((int(offsets[-1]), 2048))
+    done = 0
     with multiprocessing.get_context("spawn").Pool(nproc) as pool:
-        for r in pool.imap_unordered(expert_reference, jobs):
-            results.append(r)
-            if len(results) % 32 == 0:
-                say(f"  oracle: {len(results)} of {len(jobs)} experts done")
-    ref = np.zeros((rows.size, 2048))
-    for e, code_hash, scale_hash, ref_rows in results:
-        assert hashlib.sha256(qb[e].cpu().numpy().tobytes()).hexdigest() == code_hash, f"expert {e} codes"
-        assert hashlib.sha256(sb[e].cpu().numpy().tobytes()).hexdigest() == scale_hash, f"expert {e} scales"
-        ref[[pos[r] for r in seg_rows[e]]] = ref_rows
-    check_bf16(y[torch.from_numpy(rows).cuda()], ref, f"first/last/inner rows of all {len(jobs)} segments")
+        for e, code_hash, scale_hash, ref_rows in pool.imap_unordered(expert_reference, jobs):
+            assert hashlib.sha256(qb[e].cpu().numpy().tobytes()).hexdigest() == code_hash, f"expert {e} codes"
+            assert hashlib.sha256(sb[e].cpu().numpy().tobytes()).hexdigest() == scale_hash, f"expert {e} scales"
+            ref[int(offsets[e]):int(offsets[e + 1])] = ref_rows
+            done += 1
+            if done % 32 == 0:
+                say(f"  oracle: {done} of {len(jobs)} experts done")
+    check_bf16(y, ref, f"all {int(offsets[-1])} routed rows x 2048")
     say("  FP8 dispatch by index: quantise the 8192 tokens, gather rows inside the GEMM")
     qt, st = fp8.fp8_quant_act_1x128(tokens.cuda())
     idx = perm.to(torch.int32).cuda()
