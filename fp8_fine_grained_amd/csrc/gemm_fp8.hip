@@ -21,7 +21,9 @@
 //    grouped, else the first two), one or two
 //    DMAs per step between MFMAs: early enough to land before the end of the
 //    iteration, spread out because each DMA costs the issuing wavefront and the
-//    LDS both per instruction and per byte.
+//    LDS both per instruction and per byte.  The power-of-two tiles and the
+//    grouped FP8 tiles place each of a step's DMAs right after one of its
+//    MFMAs, in an order fixed by scheduling barriers.
 //  * Tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    issued through inline assembly together with the waits and barriers: the
 //    compiler cannot tell that an LDS read does not overlap the DMA writes still
@@ -687,6 +689,20 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     // immediate promotion.
     constexpr bool DEFER = GROUPED && !SCALED && BALIGN;
     static_assert(!DEFER || SN % 2 == 0, "the deferred partials use the buffer step 0 does not write");
+    // Interleaved issue (the four-wavefront power-of-two tiles and the grouped
+    // FP8 tiles): the step's tile DMAs are not issued together before its MFMAs
+    // but one after each MFMA, followed (fp32 scales) by the promotion of the
+    // previous step's partial for the same m sub-tile, in an order fixed by
+    // scheduling barriers.  A wavefront issues in order, so a run of DMA
+    // instructions (each with its M0 write and wait state) behind a run of
+    // MFMAs leaves the matrix core idle once the MFMAs drain; alone on its SIMD,
+    // nothing else fills that gap.  Dense 4096 x 7168 x 7168 with power-of-two
+    // scales 176.3 -> 169.0 and 179.0 -> 171.9 us (two boxes), the gathering
+    // MoE GEMM 1421.9 -> 1397.1 us, outputs bit-identical.  The fp32-scale
+    // dense tiles (189.3 vs 189.5 us) and the exact tiles (weight gradient
+    // 1609 vs 1630 us) gain nothing and keep the compiler's order.
+    constexpr bool ILV = (SCALED && NW == 4) || (GROUPED && !SCALED && !EXACT);
+    static_assert(!ILV || SCALED || (DEFER && !ROWS), "the interleaved promotion is the block-scale form");
     float f_prev[SMW];
     for (int kb = 0; kb < KB; ++kb) {
       // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
@@ -694,6 +710,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       // again: the loop body stays branch-free and every wait is the same.
       const int st_fill = st == 0 ? STAGES - 1 : st - 1;
       const int kb_fill = clampkb(kb + STAGES - 1);
+      // Interleaved issue: the j-th tile DMA of step i, if that step has one.
+      auto dma_slot = [&](int i, int j) {
+        const int d = i * ND / SPREAD + j;
+        if (i < SPREAD && d < (i + 1) * ND / SPREAD) dma_tile(d, kb_fill, st_fill);
+      };
       const uint8_t* tB = tiles + st * STAGE + TILE_A;
       if constexpr (!BALIGN) {
 #pragma unroll
@@ -711,7 +732,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
       for (int i = 0; i < SN - 1; ++i) {
         // The loads of the block being prefetched go out over the first SPREAD
         // sub-tile steps, between MFMAs.
-        if (i < SPREAD) {
+        if (!ILV && i < SPREAD) {
 #pragma unroll
           for (int d = i * ND / SPREAD; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
         }
@@ -731,7 +752,29 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
         if constexpr (SCALED) {
           const int ewi = BALIGN ? ew : e8m0(bsv(i));
 #pragma unroll
-          for (int j = 0; j < SMW; ++j) acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
+          for (int j = 0; j < SMW; ++j) {
+            acc[i][j] = mma_scaled(fn, fm[j], acc[i][j], ewi, ex[j]);
+            if constexpr (ILV) {
+              dma_slot(i, j);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else if constexpr (ILV) {
+          const WideFrag none{};
+#pragma unroll
+          for (int j = 0; j < SMW; ++j) {
+            P[i & 1][j] = partial(fn, none, j);
+            dma_slot(i, j);
+            if (i > 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = fmaf(P[(i - 1) & 1][j][r], f[j], acc[i - 1][j][r]);
+            } else if (kb > 0) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_prev[j], acc[SN - 1][j][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         } else {
           WideFrag wn_frag;
           if constexpr (EXACT) wn_frag = widen(fn);
@@ -754,6 +797,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
             promote(acc[i - 1], P[(i - 1) & 1], f, sbr[(i - 1) & 1], bsv(i > 0 ? i - 1 : 0));
           else if (DEFER && kb > 0)
             promote(acc[SN - 1], P[(SN - 1) & 1], f_prev, sbr[(SN - 1) & 1], 0.0f);
+        }
+        if constexpr (ILV) {
+          // the step's DMAs beyond its MFMA count (grouped tiles with few live rows)
+          if (i < SPREAD) {
+#pragma unroll
+            for (int d = i * ND / SPREAD + SMW; d < (i + 1) * ND / SPREAD; ++d) dma_tile(d, kb_fill, st_fill);
+          }
         }
         if constexpr (FD2) {
           fn = fn1;
