@@ -21,9 +21,10 @@
 //    grouped, else the first two), one or two
 //    DMAs per step between MFMAs: early enough to land before the end of the
 //    iteration, spread out because each DMA costs the issuing wavefront and the
-//    LDS both per instruction and per byte.  The power-of-two tiles and the
-//    grouped FP8 tiles place each of a step's DMAs right after one of its
-//    MFMAs, in an order fixed by scheduling barriers.
+//    LDS both per instruction and per byte.  The power-of-two tiles, the
+//    grouped FP8 tiles and the fp32-scale dense tiles with block scales place
+//    each of a step's DMAs right after one of its MFMAs, in an order fixed by
+//    scheduling barriers.
 //  * Tiles move global -> LDS with global_load_lds_dwordx4 (no VGPR staging),
 //    issued through inline assembly together with the waits and barriers: the
 //    compiler cannot tell that an LDS read does not overlap the DMA writes still
@@ -503,10 +504,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     if constexpr (PF > 0) dma4(pf_ptr + static_cast<int64_t>(kb_begin + kb) * 128, lds_addr(s_filler));
   };
   constexpr int ND = A_DMA + B_DMA;  // tile DMAs per wavefront per stage
-  // sub-tile steps that issue them: six of eight for the dense tiles, three of
-  // four for the grouped ones (1.6% faster on the MoE shape than two, which
+  // The fp32-scale dense tiles with block scales issue each DMA right after
+  // one MFMA (the interleaved issue described in the K loop).
+  constexpr bool ILV_DENSE = !GROUPED && !SCALED && !EXACT && !ROWS && BALIGN && NW == 8;
+  // Sub-tile steps that issue the DMAs: four of eight for those tiles (their
+  // GEMM on 4096 x 7168 x 7168: 187.9 us over six steps, 185.7 over four, 185.3
+  // over two, 188.7 in one), six of eight for the other 256 x 256 tiles, three
+  // of four for the grouped ones (1.6% faster on the MoE shape than two, which
   // the row-scaled weight-gradient tiles keep: three is 1-8% slower there)
-  constexpr int SPREAD = SN >= 7 ? SN - 2 : (SN >= 4 ? (GROUPED ? SN - 1 : SN / 2) : SN);
+  constexpr int SPREAD = ILV_DENSE ? 4 : (SN >= 7 ? SN - 2 : (SN >= 4 ? (GROUPED ? SN - 1 : SN / 2) : SN));
   auto dma_tile = [&](int d, int kb, int st) {
     const int64_t kof = static_cast<int64_t>(kb_begin + kb) * 128;
     const uint32_t so = static_cast<uint32_t>(st) * STAGE;
@@ -689,20 +695,23 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
     // immediate promotion.
     constexpr bool DEFER = GROUPED && !SCALED && BALIGN;
     static_assert(!DEFER || SN % 2 == 0, "the deferred partials use the buffer step 0 does not write");
-    // Interleaved issue (the four-wavefront power-of-two tiles and the grouped
-    // FP8 tiles): the step's tile DMAs are not issued together before its MFMAs
-    // but one after each MFMA, followed (fp32 scales) by the promotion of the
-    // previous step's partial for the same m sub-tile, in an order fixed by
-    // scheduling barriers.  A wavefront issues in order, so a run of DMA
-    // instructions (each with its M0 write and wait state) behind a run of
-    // MFMAs leaves the matrix core idle once the MFMAs drain; alone on its SIMD,
-    // nothing else fills that gap.  Dense 4096 x 7168 x 7168 with power-of-two
-    // scales 176.3 -> 169.0 and 179.0 -> 171.9 us (two boxes), the gathering
-    // MoE GEMM 1421.9 -> 1397.1 us, outputs bit-identical.  The fp32-scale
-    // dense tiles (189.3 vs 189.5 us) and the exact tiles (weight gradient
-    // 1609 vs 1630 us) gain nothing and keep the compiler's order.
-    constexpr bool ILV = (SCALED && NW == 4) || (GROUPED && !SCALED && !EXACT);
-    static_assert(!ILV || SCALED || (DEFER && !ROWS), "the interleaved promotion is the block-scale form");
+    // Interleaved issue (the four-wavefront power-of-two tiles, the grouped FP8
+    // tiles and the fp32-scale dense tiles with block scales): the step's tile
+    // DMAs are not issued together before its MFMAs but one after each MFMA,
+    // followed (fp32 scales) by the promotion of the previous step's partial
+    // for the same m sub-tile, in an order fixed by scheduling barriers.  A
+    // wavefront issues in order, so a run of DMA instructions (each with its M0
+    // write and wait state) behind a run of MFMAs leaves the matrix core idle
+    // once the MFMAs drain; alone on its SIMD, nothing else fills that gap.
+    // Dense 4096 x 7168 x 7168 with power-of-two scales 176.3 -> 169.0 and
+    // 179.0 -> 171.9 us (two boxes), the gathering MoE GEMM 1421.9 -> 1397.1
+    // us, outputs bit-identical.  The fp32-scale dense tiles gain only together
+    // with an earlier DMA spread (four steps instead of six: 188.8 -> 187.4 and
+    // 187.9 -> 185.7 us; with six, 189.3 vs 189.5).  The exact tiles (weight
+    // gradient 1609 vs 1630 us) gain nothing and keep the compiler's order.
+    constexpr bool ILV = (SCALED && NW == 4) || (GROUPED && !SCALED && !EXACT) || ILV_DENSE;
+    static_assert(!ILV || SCALED || !ROWS, "the interleaved promotion is the block-scale form");
+    static_assert(!ILV || PF == 0 || SPREAD <= SN - 2, "the L2 prefetch stays each iteration's newest load");
     float f_prev[SMW];
     for (int kb = 0; kb < KB; ++kb) {
       // Block kb+STAGES-1 goes into the stage consumed in the previous iteration.
@@ -768,7 +777,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_fp8_block_kernel(FParams
             if (i > 0) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) acc[i - 1][j][r] = fmaf(P[(i - 1) & 1][j][r], f[j], acc[i - 1][j][r]);
-            } else if (kb > 0) {
+            } else if (DEFER && kb > 0) {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 acc[SN - 1][j][r] = fmaf(P[(SN - 1) & 1][j][r], f_prev[j], acc[SN - 1][j][r]);
