@@ -140,9 +140,11 @@ def test_handworked_dequant_scale_indexing(case):
     assert np.all(deq[~listed] == 0)
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered:RuntimeWarning")
 def test_planted_mistake_fails_the_pins():
     """The fixture catches a plausible slip in the statistics: the relative
-    error taken against the dequantised value instead of the input."""
+    error taken against the dequantised value instead of the input (elements
+    flushed to zero make that ratio infinite, so its percentiles warn)."""
     def wrong_qdq(x, deq):
         x = np.asarray(x, np.float64)
         deq = np.asarray(deq, np.float64)
