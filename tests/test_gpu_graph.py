@@ -14,7 +14,7 @@ import torch
 import workloads
 from fp8_fine_grained_amd import binding as fp8
 from oracle import gemm, quant
-from tests.gpu_util import check_f32, f32, say
+from tests.gpu_util import check_bf16, check_f32, f32, say
 
 pytestmark = pytest.mark.gpu
 
@@ -109,3 +109,55 @@ def test_graph_dense_step_and_k_split_replays():
         same = float((diff == 0).float().mean())
         say(f"  K-split output: {100 * same:.1f}% of elements bit-identical")
         assert same >= 0.9  # only the 32 split tiles (32 of 544) may differ
+
+
+def test_graph_moe_gather_step_replays():
+    """An MoE step (1x128 quantisation of the tokens, then the grouped GEMM that
+    reads each routed row from its token by index, segment offsets on the
+    device) captured in a graph: no host synchronisation, so every replay
+    equals the eager step bit for bit, after eager writes to its outputs, and
+    the eager result equals the oracle's per-expert GEMMs within the bf16 bound."""
+    T, E, topk, N, K = 512, 16, 4, 256, 512
+    route = workloads.moe_routing(seed=9, T=T, E=E, topk=topk)
+    tokens = workloads.moe_tokens(seed=9, T=T, H=K).cuda()
+    w = torch.stack([workloads.moe_expert_weight(g, seed=9, N=N, K=K) for g in range(E)]).cuda()
+    qb, sb = fp8.fp8_quant_weight_128x128(w.view(E * N, K))
+    qb, sb = qb.view(E, N, K), sb.view(E, N // 128, K // 128)
+    idx = torch.from_numpy(route["perm"].astype(np.int32)).cuda()
+    off = torch.from_numpy(route["offsets"]).cuda()
+    qt = torch.empty((T, K), dtype=torch.uint8, device="cuda")
+    st = torch.empty((T, K // 128), dtype=torch.float32, device="cuda")
+    y = torch.empty((idx.numel(), N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        fp8.fp8_quant_act_1x128(tokens, qt, st)
+        fp8.fp8_block_grouped_gemm_gather(qt, st, idx, off, qb, sb, accum="fp8", y=y)
+
+    say(f"MoE gather step {T} tokens, {E} experts top-{topk}, eager")
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (qt, st, y)]
+    rt, rst = quant.quant_1x128(f32(tokens))
+    assert np.array_equal(eager[0].cpu().numpy(), rt)
+    offsets = route["offsets"]
+    perm = route["perm"]
+    ref = np.zeros((idx.numel(), N))
+    for g in range(E):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        if hi > lo:
+            rb, rsb = quant.quant_128x128(f32(w[g]))
+            ref[lo:hi] = gemm.block_gemm(rt[perm[lo:hi]], rst[perm[lo:hi]], rb, rsb)
+    check_bf16(eager[2], ref, "eager MoE step")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"replay {rep}")
+        for t_ in (qt, st, y):
+            t_.fill_(3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((qt, st, y), eager):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), f"replay {rep} differs"
