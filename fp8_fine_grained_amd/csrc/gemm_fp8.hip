@@ -17,8 +17,8 @@
 //    With 256 x 256 the L2 -> CU traffic is 64 KB per 16.8 MFLOP.
 //  * One 128-wide K block per LDS stage; the loads of block kb+STAGES-1 are in
 //    flight while block kb is multiplied.  They are issued over the first six
-//    of the eight sub-tile steps (128 x 256 tiles: the first three of four when
-//    grouped, else the first two), one or two
+//    of the eight sub-tile steps (four for the fp32-scale dense tiles; 128 x 256
+//    tiles: the first three of four when grouped, else the first two), one or two
 //    DMAs per step between MFMAs: early enough to land before the end of the
 //    iteration, spread out because each DMA costs the issuing wavefront and the
 //    LDS both per instruction and per byte.  The power-of-two tiles, the
@@ -47,7 +47,8 @@
 //    buffered so the FMAs of one sub-tile run under the MFMAs of the next.  The
 //    barrier of each K block comes right after its last LDS read: the last
 //    sub-tile's MFMAs and FMAs run after it, while the next block's fragments
-//    are being read.
+//    are being read (FP8 and scaled tiles: its n fragment and scales first,
+//    then one m fragment after each MFMA).
 //  * Dense tiles are numbered so that each XCD (workgroup id mod 8) works on one
 //    contiguous band of the tile grid, keeping its operand panels in its L2;
 //    grouped tiles are in expert-major order, so one XCD works through one
