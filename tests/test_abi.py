@@ -124,7 +124,7 @@ def test_quant_weight_dual_validation(L):
     assert f(*args(ld=260)) == fp8.ERR_MISALIGNED  # row pitch 520 B
 
 
-def test_survey_signatures_take_no_accumulation_argument(L):
+def test_basic_gemm_signatures_take_no_accumulation_argument(L):
     """fp8_block_gemm and fp8_block_grouped_gemm have the boundary's argument
     lists; their validation matches the *_accum forms with the default mode."""
     g = L.fp8_block_gemm
