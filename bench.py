@@ -762,6 +762,35 @@ def bench_moe(args, torch, fp8, workloads):
         with tp:
             fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
     torch.cuda.synchronize()
+    del qa, sa
+    # One GPU's share under expert parallelism over 8 GPUs: 32 consecutive
+    # experts and the rows routed to them (~8192), the same gathering launch at
+    # G = 32.  The eight shares of the 256 experts run in turn, so consecutive
+    # launches read different weights (470 MB each) from HBM.
+    import numpy as np
+
+    GS = G // 8
+    off_np = route["offsets"].astype(np.int64)
+    perm_np = route["perm"]
+    shares = []
+    for e in range(8):
+        lo, hi = int(off_np[e * GS]), int(off_np[(e + 1) * GS])
+        o = torch.from_numpy((off_np[e * GS:(e + 1) * GS + 1] - lo).astype(np.int32)).cuda()
+        tok = int(np.unique(perm_np[lo:hi]).size)  # distinct tokens the share reads
+        share_bytes = (tok * (K + (K // 128) * 4) + GS * (N * K + (N // 128) * (K // 128) * 4)
+                       + (hi - lo) * (N * 2 + 4))
+        shares.append((idx[lo:hi], o, qb[e * GS:(e + 1) * GS], sb[e * GS:(e + 1) * GS], y[lo:hi],
+                       2.0 * (hi - lo) * N * K, share_bytes))
+    ts = Timer(torch, args.steps)
+    s_flop = s_bytes = 0.0
+    for i in range(args.steps):
+        ix, o, b, sbs, ys, fl, by = shares[i % 8]
+        with ts:
+            fp8.fp8_block_grouped_gemm_gather(qt, st, ix, o, b, sbs, accum="fp8", y=ys)
+        s_flop += fl
+        s_bytes += by
+    torch.cuda.synchronize()
+    s_ms = sum(ts.times_ms())
     flop = 2.0 * Mt * N * K
     gms, pms = tg.mean_ms(), tp.mean_ms()
     gemm_bytes = T * K + T * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4 + Mt * N * 2 + Mt * 4
@@ -782,6 +811,12 @@ def bench_moe(args, torch, fp8, workloads):
             "fp8_quant_act_1x128 (tokens)": _hbm_line("act", tq.mean_ms() / args.steps, T * K * 3 + T * (K // 128) * 4, {}),
             "fp8_block_grouped_gemm_gather": dict(gemm_line(gms), ms_percentiles=tg.percentiles_ms()),
             "fp8_block_grouped_gemm (pre-permuted rows)": gemm_line(pms),
+            "fp8_block_grouped_gemm_gather, one GPU's expert-parallel share (32 experts, ~8192 rows; "
+            "the 8 shares in turn)": {
+                "ms": s_ms / args.steps, "TFLOP/s": s_flop / (s_ms * 1e-3) / 1e12,
+                "frac_fp8_peak": s_flop / (s_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
+                "GB/s": s_bytes / (s_ms * 1e-3) / 1e9, "frac_hbm": s_bytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "bytes": s_bytes / args.steps},
         },
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -134,6 +134,31 @@ def test_gather_small():
         assert torch.equal(y, yp), f"{accum} {dtype}"
 
 
+def test_expert_parallel_shares_equal_the_full_launch():
+    """One GPU's share under expert parallelism is the same gathering launch on a
+    contiguous range of experts (their offsets rebased to 0, their weights, the
+    index rows routed to them and the matching output rows): eight shares of 8
+    of 64 experts reproduce the full launch bit for bit."""
+    G, N, K = 64, 256, 512
+    g, ref, M = _gather_case(T=512, G=G, topk=8, N=N, K=K, seed=41)
+    qt, st, idx, off, qb, sb = g
+    say(f"expert-parallel shares: 512 tokens, {G} experts top-8 -> {M} rows, 8 shares of {G // 8}")
+    y = fp8.fp8_block_grouped_gemm_gather(qt, st, idx, off, qb, sb, accum="fp8", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    check_bf16(y, ref, "full launch")
+    off_np = off.cpu().numpy()
+    buf, ys = guarded((M, N), torch.bfloat16)
+    GS = G // 8
+    for e in range(8):
+        lo, hi = int(off_np[e * GS]), int(off_np[(e + 1) * GS])
+        o = torch.from_numpy((off_np[e * GS:(e + 1) * GS + 1] - lo).astype(np.int32)).cuda()
+        fp8.fp8_block_grouped_gemm_gather(qt, st, idx[lo:hi], o, qb[e * GS:(e + 1) * GS], sb[e * GS:(e + 1) * GS],
+                                          accum="fp8", y=ys[lo:hi])
+    torch.cuda.synchronize()
+    check_guard(buf)
+    assert torch.equal(ys, y)
+
+
 def test_gather_repeated_and_unused_tokens():
     # every routed row is token 5 or token 0; most tokens are never read
     T, K, N, G = 40, 256, 256, 3
