@@ -17,11 +17,11 @@ dual weight quantiser, each rotated the same way.  Before the W warm-up steps
 the step runs back to back for --settle seconds (default 1): a cold GPU's
 clocks take ~100 GEMMs to come up, which a long training run never sees.
 
-Other workloads (``--workload quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor``) measure the
+Other workloads (``--workload quant|moe|moe_ep|wgrad|dgrad|pow2|fused|tiny|pertensor``) measure the
 remaining rows of the path and print their own JSON line; the default run prints exactly one line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
-                    [--workload dense|quant|moe|wgrad|dgrad|pow2|fused|tiny|pertensor] [--no-cpu-baseline]
+                    [--workload dense|quant|moe|moe_ep|wgrad|dgrad|pow2|fused|tiny|pertensor] [--no-cpu-baseline]
 """
 
 import argparse
@@ -762,35 +762,6 @@ def bench_moe(args, torch, fp8, workloads):
         with tp:
             fp8.fp8_block_grouped_gemm(qa, sa, offsets, qb, sb, accum="fp8", y=y)
     torch.cuda.synchronize()
-    del qa, sa
-    # One GPU's share under expert parallelism over 8 GPUs: 32 consecutive
-    # experts and the rows routed to them (~8192), the same gathering launch at
-    # G = 32.  The eight shares of the 256 experts run in turn, so consecutive
-    # launches read different weights (470 MB each) from HBM.
-    import numpy as np
-
-    GS = G // 8
-    off_np = route["offsets"].astype(np.int64)
-    perm_np = route["perm"]
-    shares = []
-    for e in range(8):
-        lo, hi = int(off_np[e * GS]), int(off_np[(e + 1) * GS])
-        o = torch.from_numpy((off_np[e * GS:(e + 1) * GS + 1] - lo).astype(np.int32)).cuda()
-        tok = int(np.unique(perm_np[lo:hi]).size)  # distinct tokens the share reads
-        share_bytes = (tok * (K + (K // 128) * 4) + GS * (N * K + (N // 128) * (K // 128) * 4)
-                       + (hi - lo) * (N * 2 + 4))
-        shares.append((idx[lo:hi], o, qb[e * GS:(e + 1) * GS], sb[e * GS:(e + 1) * GS], y[lo:hi],
-                       2.0 * (hi - lo) * N * K, share_bytes))
-    ts = Timer(torch, args.steps)
-    s_flop = s_bytes = 0.0
-    for i in range(args.steps):
-        ix, o, b, sbs, ys, fl, by = shares[i % 8]
-        with ts:
-            fp8.fp8_block_grouped_gemm_gather(qt, st, ix, o, b, sbs, accum="fp8", y=ys)
-        s_flop += fl
-        s_bytes += by
-    torch.cuda.synchronize()
-    s_ms = sum(ts.times_ms())
     flop = 2.0 * Mt * N * K
     gms, pms = tg.mean_ms(), tp.mean_ms()
     gemm_bytes = T * K + T * (K // 128) * 4 + G * N * K + G * (N // 128) * (K // 128) * 4 + Mt * N * 2 + Mt * 4
@@ -811,18 +782,85 @@ def bench_moe(args, torch, fp8, workloads):
             "fp8_quant_act_1x128 (tokens)": _hbm_line("act", tq.mean_ms() / args.steps, T * K * 3 + T * (K // 128) * 4, {}),
             "fp8_block_grouped_gemm_gather": dict(gemm_line(gms), ms_percentiles=tg.percentiles_ms()),
             "fp8_block_grouped_gemm (pre-permuted rows)": gemm_line(pms),
-            "fp8_block_grouped_gemm_gather, one GPU's expert-parallel share (32 experts, ~8192 rows; "
-            "the 8 shares in turn)": {
-                "ms": s_ms / args.steps, "TFLOP/s": s_flop / (s_ms * 1e-3) / 1e12,
-                "frac_fp8_peak": s_flop / (s_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS,
-                "GB/s": s_bytes / (s_ms * 1e-3) / 1e9, "frac_hbm": s_bytes / (s_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "bytes": s_bytes / args.steps},
         },
         "roofline": {"bound": "hbm", "achieved": gemm_bytes / (gms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": gemm_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "traffic": _traffic("grouped_gemm_moe_65536x2048x7168_traffic.md",
                                          os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip")),
                      "mfma_counters": _mfma_counters("grouped_gemm_moe_65536x2048x7168_mfma_util.md")},
+    }
+
+
+def bench_moe_ep(args, torch, fp8, workloads):
+    # One GPU's share of the MoE up-projection under expert parallelism over 8
+    # GPUs: 32 consecutive experts and the rows routed to them (~8192 of the
+    # 65536), the same gathering launch at G = 32.  The eight shares of the 256
+    # experts run in turn, so consecutive launches read different weights (470 MB
+    # each) from HBM, as each GPU's own share would be.
+    import numpy as np
+
+    route = workloads.moe_routing()
+    tokens = workloads.moe_tokens().cuda()
+    idx = torch.from_numpy(route["perm"].astype("int32")).cuda()
+    G, N, K, GS = 256, 2048, 7168, 32
+    T, Mt = tokens.shape[0], idx.numel()
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    w = (torch.randn((G * N, K), generator=gen, device="cuda", dtype=torch.float32) * 0.02).to(torch.bfloat16)
+    qb, sb = fp8.fp8_quant_weight_128x128(w)
+    del w
+    qb, sb = qb.view(G, N, K), sb.view(G, N // 128, K // 128)
+    qt, st = fp8.fp8_quant_act_1x128(tokens)
+    y = torch.empty((Mt, N), dtype=torch.bfloat16, device="cuda")
+    off_np = route["offsets"].astype(np.int64)
+    shares = []
+    for e in range(G // GS):
+        lo, hi = int(off_np[e * GS]), int(off_np[(e + 1) * GS])
+        o = torch.from_numpy((off_np[e * GS:(e + 1) * GS + 1] - lo).astype(np.int32)).cuda()
+        tok = int(np.unique(route["perm"][lo:hi]).size)  # distinct tokens the share reads
+        nbytes = (tok * (K + (K // 128) * 4) + GS * (N * K + (N // 128) * (K // 128) * 4)
+                  + (hi - lo) * (N * 2 + 4))
+        shares.append((idx[lo:hi], o, qb[e * GS:(e + 1) * GS], sb[e * GS:(e + 1) * GS], y[lo:hi],
+                       2.0 * (hi - lo) * N * K, nbytes, hi - lo))
+
+    def launch(i):
+        ix, o, b, sbs, ys = shares[i % len(shares)][:5]
+        fp8.fp8_block_grouped_gemm_gather(qt, st, ix, o, b, sbs, accum="fp8", y=ys)
+
+    settle_clocks(torch, lambda i, t: launch(i), args.settle)
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ts = Timer(torch, args.steps)
+    flop = nbytes = 0.0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        with ts:
+            launch(i)
+        flop += shares[i % len(shares)][5]
+        nbytes += shares[i % len(shares)][6]
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    ms = ts.mean_ms()
+    flop, nbytes = flop / args.steps, nbytes / args.steps
+    rows = [sh[7] for sh in shares]
+    return {
+        "metric": "grouped FP8 GEMM TFLOP/s, one GPU's expert-parallel share", "value": flop / dt / 1e12,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": dt * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "e4m3", "data": "synthetic",
+        "config": {"workload": "one GPU's share of the MoE up-projection under 8-way expert parallelism: 32 of "
+                               "the 256 experts (W [2048,7168] each) and the rows routed to them by the top-8 "
+                               "routing of 8192 tokens; gathering grouped GEMM at G = 32, bf16 out; the eight "
+                               "shares launched in turn",
+                   "G": GS, "rows_per_share": [min(rows), max(rows)], "N": N, "K": K, "T": T},
+        "kernels": {
+            "fp8_block_grouped_gemm_gather (G = 32)": dict(
+                {"ms": ms, "TFLOP/s": flop / (ms * 1e-3) / 1e12, "frac_fp8_peak": flop / (ms * 1e-3) / 1e12 /
+                 PEAK_FP8_TFLOPS, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                 "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": nbytes},
+                ms_percentiles=ts.percentiles_ms()),
+        },
+        "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None},
     }
 
 
@@ -965,7 +1003,7 @@ def main():
     # Back-to-back steps before the warm-up, by wall time: the clock ramp of a
     # cold GPU is not part of a training step's steady rate.
     ap.add_argument("--settle", type=float, default=1.0, help="seconds of untimed steps before the warm-up")
-    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "wgrad", "dgrad", "pow2", "fused", "tiny", "pertensor"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "quant", "moe", "moe_ep", "wgrad", "dgrad", "pow2", "fused", "tiny", "pertensor"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -985,7 +1023,7 @@ def main():
     import fp8_fine_grained_amd.binding as fp8
     import workloads
 
-    fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "wgrad": bench_wgrad,
+    fn = {"dense": bench_dense, "quant": bench_quant, "moe": bench_moe, "moe_ep": bench_moe_ep, "wgrad": bench_wgrad,
           "dgrad": bench_dgrad, "pow2": bench_pow2,
           "fused": bench_fused, "tiny": bench_tiny, "pertensor": bench_pertensor}[args.workload]
     out = fn(args, torch, fp8, workloads)
