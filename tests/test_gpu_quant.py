@@ -56,7 +56,20 @@ def _special_tiles():
                                             else 2 * np.resize(mids, 125)).astype(np.float32)
     rows.append(ties)
     rows.append(-ties)
-    for j in (-1, 3, 12, -60, 90):  # pad to 16 rows (the transposed path needs M % 8 == 0)
+    for j in (-1, 3, 12, -60, 90):
+        rows.append(rng.standard_t(2.5, size=1024).astype(np.float32) * np.float32(2.0 ** j))
+    # The ends of the scale range the contract allows: every group's amax exactly
+    # 448 * 2^-126 (s = 2^-126, the smallest normal fp32, its other elements down
+    # in the fp32 subnormals), and exactly the largest finite bf16, 0x7F7F (so
+    # that the bf16 copy of the row is finite too).
+    for top in (np.float32(448.0 * 2.0 ** -126), np.uint32(0x7F7F0000).view(np.float32)):
+        r = base.copy().reshape(8, 128)
+        r = r / np.abs(r).max(axis=1, keepdims=True)
+        r = (r.astype(np.float64) * np.float64(top)).astype(np.float32)
+        i = np.abs(r).argmax(axis=1)
+        r[np.arange(8), i] = np.copysign(top, r[np.arange(8), i])
+        rows.append(r.reshape(1024))
+    for j in (-5, 20, 60, -100, 110, 1):  # pad to 24 rows (the transposed path needs M % 8 == 0)
         rows.append(rng.standard_t(2.5, size=1024).astype(np.float32) * np.float32(2.0 ** j))
     return np.stack(rows)
 
