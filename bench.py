@@ -860,7 +860,10 @@ def bench_moe_ep(args, torch, fp8, workloads):
                 ms_percentiles=ts.percentiles_ms()),
         },
         "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None},
+                     "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "traffic": _traffic("moe_ep_share_32x2048x7168_traffic.md",
+                                         os.path.join(ROOT, "fp8_fine_grained_amd", "csrc", "gemm_fp8.hip")),
+                     "mfma_counters": _mfma_counters("moe_ep_share_32x2048x7168_mfma_util.md")},
     }
 
 
