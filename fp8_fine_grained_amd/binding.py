@@ -41,6 +41,8 @@ _SIGS = {
                              _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_void_p],
     "fp8_quant_weight_128x128_dual": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
                                       _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
+    "fp8_quant_weight_128x128_dual_pow2": [_c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64,
+                                           _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p],
     "fp8_block_gemm": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int,
                        _c.c_void_p, _c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p],
     "fp8_block_gemm_accum": [_c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_int, _c.c_int,
@@ -208,11 +210,12 @@ def fp8_quant_per_tensor(x, layout="act", q=None, scales=None, stream=None):
     return q, scales
 
 
-def fp8_quant_weight_128x128_dual(w, q=None, scales=None, q_t=None, scales_t=None, stream=None):
+def fp8_quant_weight_128x128_dual(w, q=None, scales=None, q_t=None, scales_t=None, stream=None, pow2=False):
     """128x128 quantisation of ``w`` [N, K] plus the transposed operand.
 
     Returns ``(q [N, K], scales [N/128, K/128], q_t [K, N], scales_t [K/128, N/128])``;
-    ``(q_t, scales_t)`` is the B operand of the data-gradient GEMM dX = dY W."""
+    ``(q_t, scales_t)`` is the B operand of the data-gradient GEMM dX = dY W.
+    ``pow2=True`` calls fp8_quant_weight_128x128_dual_pow2 (power-of-two scales)."""
     _on_gpu(w)
     N, K = w.shape
     if w.stride(1) != 1:
@@ -223,9 +226,10 @@ def fp8_quant_weight_128x128_dual(w, q=None, scales=None, q_t=None, scales_t=Non
     q_t = torch.empty((K, N), dtype=torch.uint8, device=dev) if q_t is None else q_t
     scales_t = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev) if scales_t is None else scales_t
     _on_gpu(q, scales, q_t, scales_t)
-    st = lib().fp8_quant_weight_128x128_dual(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(q),
-                                             _ptr(scales), _ptr(q_t), _ptr(scales_t), _stream(stream))
-    _check("fp8_quant_weight_128x128_dual", st)
+    fn = "fp8_quant_weight_128x128_dual_pow2" if pow2 else "fp8_quant_weight_128x128_dual"
+    st = getattr(lib(), fn)(_ptr(w), _dtype_code(w.dtype), N, K, w.stride(0), _ptr(q), _ptr(scales), _ptr(q_t),
+                            _ptr(scales_t), _stream(stream))
+    _check(fn, st)
     return q, scales, q_t, scales_t
 
 

@@ -162,9 +162,10 @@ int fp8_quant_per_tensor(const void* x, int x_dtype, int64_t M, int64_t K, int64
                                                    static_cast<hipStream_t>(stream)));
 }
 
-int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
-                                  uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
-                                  fp8fg_stream_t stream) {
+namespace {
+
+int quant_weight_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w, uint8_t* q, float* scales,
+                      uint8_t* q_t, float* scales_t, bool pow2, fp8fg_stream_t stream) {
   if (!valid_dtype(w_dtype) || N < 0 || K < 0) return FP8FG_ERR_INVALID_ARG;
   if (N == 0 || K == 0) return FP8FG_OK;
   if (N % 128 != 0 || K % 128 != 0) return FP8FG_ERR_UNSUPPORTED;
@@ -174,8 +175,22 @@ int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t
   if (!aligned(w, 16) || !aligned(q, 16) || !aligned(q_t, 16) || !aligned(scales, 4) || !aligned(scales_t, 4) ||
       (ld_w * elem_size(w_dtype)) % 16 != 0)
     return FP8FG_ERR_MISALIGNED;
-  return hip_status(fp8fg::launch_quant_weight_dual(w, w_dtype == FP8FG_BF16, N, K, ld_w, q, scales, q_t, scales_t,
-                                                    static_cast<hipStream_t>(stream)));
+  return hip_status(fp8fg::launch_quant_weight_dual(w, w_dtype == FP8FG_BF16, pow2, N, K, ld_w, q, scales, q_t,
+                                                    scales_t, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                  uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
+                                  fp8fg_stream_t stream) {
+  return quant_weight_dual(w, w_dtype, N, K, ld_w, q, scales, q_t, scales_t, false, stream);
+}
+
+int fp8_quant_weight_128x128_dual_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                       uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
+                                       fp8fg_stream_t stream) {
+  return quant_weight_dual(w, w_dtype, N, K, ld_w, q, scales, q_t, scales_t, true, stream);
 }
 
 namespace {

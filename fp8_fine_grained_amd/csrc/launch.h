@@ -27,7 +27,7 @@ hipError_t launch_quant_act_weight(const void* x, bool x_bf16, int64_t M, int64_
                                    float* s_x, const void* w, bool w_bf16, int64_t N, int64_t K_w, int64_t ld_w,
                                    uint8_t* q_w, float* s_w, bool pow2, hipStream_t s);
 // 128x128 quantisation writing q [N,K] and the transposed q_t [K,N] (+ scales, scales_t).
-hipError_t launch_quant_weight_dual(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+hipError_t launch_quant_weight_dual(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, int64_t ld,
                                     uint8_t* q, float* scales, uint8_t* qt, float* scales_t, hipStream_t s);
 
 struct GemmArgs {

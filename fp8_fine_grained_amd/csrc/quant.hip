@@ -461,7 +461,7 @@ __device__ __forceinline__ void transpose4x4(const uint32_t (&r4)[4], uint32_t (
 // columns; a 4x4 byte transpose) into an LDS tile of the transposed block,
 // whose 32-dword rows c are XOR-permuted by ((c / L) & 3) << 3 (two lanes per
 // bank at most), and the tile leaves as full 128-byte rows.
-template <bool BF16>
+template <bool BF16, bool POW2>
 __global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __restrict__ w, int64_t ld, int GK, int GN,
                                                                 uint8_t* __restrict__ q, float* __restrict__ scales,
                                                                 uint8_t* __restrict__ qt, float* __restrict__ scales_t,
@@ -489,7 +489,7 @@ __global__ void __launch_bounds__(256) quant_weight_dual_kernel(const void* __re
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   float s, inv;
-  group_scale(amax, s, inv);
+  group_scale<POW2>(amax, s, inv);
   uint32_t codes[4][4];  // [row rr][dword d]: elements 4d .. 4d+3 of the thread's 16
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
@@ -622,16 +622,17 @@ hipError_t launch_quant_act_weight(const void* x, bool x_bf16, int64_t M, int64_
   return hipGetLastError();
 }
 
-hipError_t launch_quant_weight_dual(const void* w, bool bf16, int64_t N, int64_t K, int64_t ld,
+hipError_t launch_quant_weight_dual(const void* w, bool bf16, bool pow2, int64_t N, int64_t K, int64_t ld,
                                     uint8_t* q, float* scales, uint8_t* qt, float* scales_t, hipStream_t s) {
   const int GK = static_cast<int>(K / 128), GN = static_cast<int>(N / 128);
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(GN) * GK));
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, w, ld, GK, GN, q, scales, qt, scales_t, N, K);
+  };
   if (bf16)
-    hipLaunchKernelGGL(quant_weight_dual_kernel<true>, grid, dim3(256), 0, s, w, ld, GK, GN, q, scales, qt, scales_t,
-                       N, K);
+    pow2 ? go(quant_weight_dual_kernel<true, true>) : go(quant_weight_dual_kernel<true, false>);
   else
-    hipLaunchKernelGGL(quant_weight_dual_kernel<false>, grid, dim3(256), 0, s, w, ld, GK, GN, q, scales, qt,
-                       scales_t, N, K);
+    pow2 ? go(quant_weight_dual_kernel<false, true>) : go(quant_weight_dual_kernel<false, false>);
   return hipGetLastError();
 }
 

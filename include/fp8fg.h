@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FP8FG_ABI_VERSION 8
+#define FP8FG_ABI_VERSION 9
 
 /* Status codes returned by every entry point. */
 enum {
@@ -221,6 +221,11 @@ int fp8_quant_act_weight(const void* x, int x_dtype, int64_t M, int64_t K_x, int
 int fp8_quant_weight_128x128_dual(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
                                   uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
                                   fp8fg_stream_t stream);
+/* The same with power-of-two block scales (rule as fp8_quant_act_1x128_pow2),
+ * for the data gradient on the scaled MFMA (FP8FG_ACCUM_SCALED_MFMA). */
+int fp8_quant_weight_128x128_dual_pow2(const void* w, int w_dtype, int64_t N, int64_t K, int64_t ld_w,
+                                       uint8_t* q, float* scales, uint8_t* q_t, float* scales_t,
+                                       fp8fg_stream_t stream);
 
 /*
  * Block-scaled FP8 GEMM  Y = deq(A) * deq(B)^T  (innerforce accumulation

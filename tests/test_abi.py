@@ -21,7 +21,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = fp8.declared_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_1x128_pow2", "fp8_quant_weight_128x128",
-                          "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual", "fp8_quant_per_tensor",
+                          "fp8_quant_weight_128x128_pow2", "fp8_quant_weight_128x128_dual",
+                          "fp8_quant_weight_128x128_dual_pow2", "fp8_quant_per_tensor",
                           "fp8_quant_act_weight",
                           "fp8_block_gemm", "fp8_block_gemm_accum", "fp8_block_gemm_quant", "fp8_block_grouped_gemm",
                           "fp8_block_grouped_gemm_accum", "fp8_block_grouped_gemm_gather",
@@ -31,7 +32,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.fp8fg_abi_version() == 8
+    assert L.fp8fg_abi_version() == 9
     for st in range(0, 6):
         assert L.fp8fg_status_string(st)
     assert b"unknown" in L.fp8fg_status_string(99)
@@ -107,8 +108,9 @@ def test_quant_act_weight_validation(L):
     assert f(*args(x=NULL, M=0, qx=NULL, sx=NULL, N=100)) == fp8.ERR_UNSUPPORTED
 
 
-def test_quant_weight_dual_validation(L):
-    f = L.fp8_quant_weight_128x128_dual
+@pytest.mark.parametrize("fn", ["fp8_quant_weight_128x128_dual", "fp8_quant_weight_128x128_dual_pow2"])
+def test_quant_weight_dual_validation(L, fn):
+    f = getattr(L, fn)
     ok = dict(w=GOOD, dt=fp8.BF16, N=128, K=256, ld=256, q=GOOD, s=GOOD, qt=GOOD, st=GOOD, stream=NULL)
     args = lambda **kw: [kw.get(k, v) for k, v in ok.items()]
     assert f(*args(dt=7)) == fp8.ERR_INVALID_ARG

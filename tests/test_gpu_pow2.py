@@ -70,6 +70,41 @@ def test_weight():
         assert_scales_equal(s, s_ref, what)
 
 
+def test_weight_dual_and_data_gradient():
+    """The dual quantiser with power-of-two scales: W and W^T codes and scales
+    bit-exact against the oracle (W^T quantised on its own), and the data
+    gradient dX = dY W on the scaled MFMA within the FP8 bound."""
+    d = workloads.dgrad(M=200, N=384, K=768)  # dX [200, 768]: the scaled MFMA needs 256 | 768
+    dy, w = d["dy"], d["w"]
+    N, K = w.shape
+    wpad = torch.zeros((N, K + 64), dtype=w.dtype)
+    wpad[:, :K] = w  # row pitch K + 64
+    say(f"pow2 dual quantiser {tuple(w.shape)} (pitch {K + 64}) and the scaled data gradient")
+    bufs = [guarded(sh, dt) for sh, dt in (((N, K), torch.uint8), ((N // 128, K // 128), torch.float32),
+                                           ((K, N), torch.uint8), ((K // 128, N // 128), torch.float32))]
+    q, s, qt, st = (b[1] for b in bufs)
+    fp8.fp8_quant_weight_128x128_dual(wpad.cuda()[:, :K], q, s, qt, st, pow2=True)
+    torch.cuda.synchronize()
+    for b in bufs:
+        check_guard(b[0])
+    rq, rs = quant.quant_128x128(f32(w), scale="pow2")
+    rqt, rst = quant.quant_128x128(np.ascontiguousarray(f32(w).T), scale="pow2")
+    assert_codes_equal(q, rq, "codes")
+    assert_scales_equal(s, rs, "scales")
+    assert_codes_equal(qt, rqt, "transposed codes")
+    assert_scales_equal(st, rst, "transposed scales")
+    qa, sa = fp8.fp8_quant_act_1x128(dy.cuda(), pow2=True)
+    ra, rsa = quant.quant_1x128(f32(dy), scale="pow2")
+    assert np.array_equal(qa.cpu().numpy(), ra) and np.array_equal(sa.cpu().numpy(), rsa)
+    y = fp8.fp8_block_gemm(qa, sa, qt, st, accum="scaled", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = gemm.block_gemm(ra, rsa, rqt, rst)
+    bound = fp8_mfma_bound(ra, rsa, rqt, rst, "block")
+    y = f32(y).astype(np.float64)
+    say(f"  dX fp32: Frobenius {frob_rel(y, ref):.3e}, max err/bound {np.max(np.abs(y - ref) / bound):.3f}")
+    assert np.all(np.isfinite(y)) and np.all(np.abs(y - ref) <= bound)
+
+
 def _operands(x_cpu, w_cpu):
     qa, sa = fp8.fp8_quant_act_1x128(x_cpu.cuda(), pow2=True)
     qb, sb = fp8.fp8_quant_weight_128x128(w_cpu.cuda(), pow2=True)
