@@ -48,10 +48,13 @@ struct Params {
 };
 
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values rounded to nearest-even bf16 and packed (low half a): one
+// v_cvt_pk_bf16_f32 on gfx950, bit-identical to the integer rounding
+// ((u + 0x7FFF + lsb) >> 16) for finite values.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ v8h widen8(uint32_t lo, uint32_t hi) {
@@ -293,8 +296,8 @@ __global__ void __launch_bounds__(WM* WN * 64) gemm_kernel(Params p) {
       const int64_t n = n0 + wn * TN + i * 16 + 4 * (lane >> 4);
       if constexpr (BF16OUT) {
         u32x2 o;
-        o[0] = bf16_rne(acc[i][j][0]) | (bf16_rne(acc[i][j][1]) << 16);
-        o[1] = bf16_rne(acc[i][j][2]) | (bf16_rne(acc[i][j][3]) << 16);
+        o[0] = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+        o[1] = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.y) + m * p.N + n) = o;
       } else {
         *reinterpret_cast<v4f*>(static_cast<float*>(p.y) + m * p.N + n) = acc[i][j];
